@@ -1,0 +1,271 @@
+"""CPU oracle of the MoE verify step.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this module.  The GPU library never calls it and it imports
+nothing from the GPU library; the two share only the seeded input arrays.
+
+What it computes, and from where
+--------------------------------
+The decoder is the one on "Jina AI Releases jina-ocr-v1, a 3.4B MoE Document
+Parser With Built-In Speculative Decoding" (ainewsfeed.tech), architecture
+paragraph: a stack of MoE layers with 64 routed experts, two always-on shared
+experts and top-6 routing.  Its FastMTP paragraph fixes the verify rule: the
+decoder's own greedy choice at every position, acceptance of the longest
+draft prefix that matches those choices, and one more token committed by the
+decoder itself (a bonus token when every draft matched), so that the
+committed text is exactly what plain greedy decoding would produce.  The
+modelscope.ai paper page ("Jina-OCR-v1: Efficient Document Parsing with
+Speculative Decoding and Dense Verifiable Rewards", Abstract) gives K = 3 and
+that greedy verification is lossless.
+
+Readings where the pages are silent (each listed with its reason in the
+design notes): SwiGLU experts, a = SiLU(gate) * up; RMSNorm with eps 1e-6 and
+order (h * inv) * gamma; the router is a linear map to 64 logits, selection is
+on logits, ties go to the lower expert id, gates are the softmax over the 6
+chosen logits; shared experts have weight 1; each layer is h <- h + MoE(RMSNorm(h));
+a final RMSNorm precedes the LM head; argmax ties go to the lowest token id.
+
+Precision
+---------
+All arithmetic is float64.  Values the kernel *stores* in the model's dtype
+are rounded to it, through fp32, exactly where the kernel rounds: the hidden
+state between layers, the normalised input x of each layer, the SwiGLU
+product a, and the final normalised x_f.  Router logits and LM-head logits
+are rounded to fp32 (the precision the kernel holds them in) before the
+integer decisions taken on them (top-6, argmax), and the decision margins are
+measured on those fp32 values.  Everything else stays float64.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(library special cases, closed forms, invariants, brute force, and the
+lossless greedy-equivalence property).
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored tensor -> float64.  bf16 tensors arrive as uint16 bit patterns."""
+    if dtype == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def fp32_to_bf16_rne(v32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    bf16 keeps the top 16 bits of the fp32 pattern.  Adding 0x7FFF plus the
+    lowest kept bit to the pattern before truncating rounds to nearest with
+    ties going to the even kept value.  NaNs stay NaN (quiet bit forced).
+    """
+    u = np.ascontiguousarray(v32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint32)
+    nan = np.isnan(np.asarray(v32, dtype=np.float32))
+    r = np.where(nan, (u >> np.uint64(16)).astype(np.uint32) | np.uint32(0x40), r)
+    return r.astype(np.uint16)
+
+
+def store(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a float64 value to the model's storage dtype (via fp32), returned
+    as float64 so the next step computes on exactly the stored value."""
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return v32.astype(np.float64)
+    if dtype == "bf16":
+        return widen(fp32_to_bf16_rne(v32), "bf16")
+    raise ValueError(dtype)
+
+
+def as_fp32(v: np.ndarray) -> np.ndarray:
+    """Round to fp32 and return as float64 (decision precision of the kernel)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# the per-layer steps
+# ---------------------------------------------------------------------------
+
+
+def rms_norm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row: (h * (mean(h^2) + eps)^(-1/2)) * gamma."""
+    h = np.asarray(h, dtype=np.float64)
+    inv = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+    return (h * inv) * gamma
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  bias: Optional[np.ndarray]) -> np.ndarray:
+    """Router logits l = x W_r^T (+ b), returned rounded to fp32."""
+    l = x @ w_router.T
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float64)
+    return as_fp32(l)
+
+
+def select_top_k(l32: np.ndarray, k: int):
+    """Top-k of one token's logits.
+
+    Experts are ordered by (logit descending, expert id ascending) and the
+    first k are kept, in that order.  The margin is the gap between the k-th
+    and (k+1)-th logit of that order (0 for an exact tie across the cut).
+    """
+    order = sorted(range(len(l32)), key=lambda e: (-l32[e], e))
+    sel = order[:k]
+    margin = float(l32[order[k - 1]] - l32[order[k]]) if len(order) > k else np.inf
+    return sel, margin
+
+
+def gate_weights(l_sel: np.ndarray) -> np.ndarray:
+    """Softmax over the selected logits (equal to the softmax over all experts
+    renormalised to the selected ones)."""
+    l_sel = np.asarray(l_sel, dtype=np.float64)
+    z = np.exp(l_sel - np.max(l_sel))
+    return z / np.sum(z)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z / (1 + e^-z)."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
+                  dtype: str) -> np.ndarray:
+    """One SwiGLU expert on rows x [m, d]: gate rows [0, F) and up rows [F, 2F)
+    of w_gate_up [2F, d]; a = SiLU(gate) * up is stored in the model dtype;
+    y = a W_down^T with w_down [d, F]."""
+    F = w_gate_up.shape[0] // 2
+    g = x @ w_gate_up[:F].T
+    u = x @ w_gate_up[F:].T
+    a = store(silu(g) * u, dtype)
+    return a @ w_down.T
+
+
+def moe_layer(h: np.ndarray, W: Dict[str, Optional[np.ndarray]], layer: int,
+              dims) -> Dict[str, np.ndarray]:
+    """One layer h_out = h + MoE(RMSNorm(h)) for every row of h [T, d]
+    (float64 holding stored values).  Rows are independent.
+
+    Returns h_out (stored values), x, logits (fp32), ids [T,k] in selection
+    order, gates [T,k], y (float64 MoE output before the residual) and the
+    per-token top-k margin.
+    """
+    dt, k, S = dims.dtype, dims.top_k, dims.n_shared
+    E, eps = dims.n_routed, dims.rms_eps
+    T, d = h.shape
+    gamma = widen(W["ffn_norm"][layer], dt)
+    x = store(rms_norm(h, gamma, eps), dt)
+    bias = None if W.get("router_b") is None else W["router_b"][layer]
+    l32 = router_logits(x, widen(W["router_w"][layer], dt), bias)
+
+    ids = np.zeros((T, k), np.int64)
+    gates = np.zeros((T, k))
+    margin = np.zeros(T)
+    for t in range(T):
+        sel, margin[t] = select_top_k(l32[t], k)
+        ids[t] = sel
+        gates[t] = gate_weights(l32[t, sel])
+
+    # slot[t, s] = contribution of the s-th selected expert (gate applied);
+    # slots k.. are the shared experts.  Each expert runs on the rows that
+    # selected it; each row is computed exactly as for a token alone.
+    slot = np.zeros((T, k + S, d))
+    for e in range(E):
+        rows, pos = np.nonzero(ids == e)
+        if rows.size == 0:
+            continue
+        y_e = swiglu_expert(x[rows], widen(W["w_gate_up"][layer, e], dt),
+                            widen(W["w_down"][layer, e], dt), dt)
+        slot[rows, pos] = gates[rows, pos][:, None] * y_e
+    for s in range(S):
+        slot[:, k + s] = swiglu_expert(x, widen(W["ws_gate_up"][layer, s], dt),
+                                       widen(W["ws_down"][layer, s], dt), dt)
+
+    y = np.zeros((T, d))
+    for s in range(k + S):          # fixed order: routed slots, then shared
+        y = y + slot[:, s]
+    h_out = store(h + y, dt)
+    return dict(h_out=h_out, x=x, logits=l32, ids=ids, gates=gates, y=y,
+                margin=margin)
+
+
+def lm_head_argmax(h: np.ndarray, final_norm: np.ndarray, lm_head: np.ndarray,
+                   dims, chunk: int = 16384) -> Dict[str, np.ndarray]:
+    """Final RMSNorm, LM-head logits z = x_f W_lm^T (fp32 for the decision),
+    greedy choice g = lowest id among the maximal logits, and the margin
+    between the largest and second-largest logit."""
+    dt = dims.dtype
+    xf = store(rms_norm(h, widen(final_norm, dt), dims.rms_eps), dt)
+    V = lm_head.shape[0]
+    z = np.empty((h.shape[0], V))
+    for v0 in range(0, V, chunk):       # the matrix is widened piecewise
+        z[:, v0:v0 + chunk] = xf @ widen(lm_head[v0:v0 + chunk], dt).T
+    z32 = as_fp32(z)
+    zmax = z32.max(axis=1)
+    g = np.array([int(np.flatnonzero(z32[t] == zmax[t])[0]) for t in range(len(zmax))],
+                 dtype=np.int64)
+    top2 = np.sort(z32, axis=1)[:, -2:] if V > 1 else np.repeat(z32, 2, axis=1)
+    return dict(xf=xf, argmax=g, margin=top2[:, 1] - top2[:, 0])
+
+
+def spec_accept(argmax: np.ndarray, drafts: np.ndarray):
+    """Greedy verification of K drafts per sequence.
+
+    argmax [B, K+1]: the decoder's choice after the committed token (position
+    0) and after each draft (positions 1..K).  Draft j is accepted when it and
+    every earlier draft equal the decoder's choice at the same position.  With
+    n accepted drafts the committed tokens are argmax[b, 0..n] (the n accepted
+    drafts themselves, then the decoder's own token: a correction, or a bonus
+    when n = K), padded with -1.
+    """
+    argmax = np.asarray(argmax)
+    drafts = np.asarray(drafts)
+    B, K = drafts.shape
+    n_acc = np.zeros(B, np.int64)
+    committed = np.full((B, K + 1), -1, np.int64)
+    for b in range(B):
+        n = 0
+        while n < K and drafts[b, n] == argmax[b, n]:
+            n += 1
+        n_acc[b] = n
+        committed[b, :n + 1] = argmax[b, :n + 1]
+    return n_acc, committed, n_acc + 1
+
+
+def forward_tokens(h_in: np.ndarray, W, dims, n_layers: Optional[int] = None,
+                   lm_head: bool = True) -> Dict[str, object]:
+    """The verify step's forward for any set of token rows (rows are
+    independent): the MoE stack, then optionally the final norm + LM argmax."""
+    L = dims.n_layers if n_layers is None else n_layers
+    h = widen(h_in, dims.dtype)
+    layers: List[Dict[str, np.ndarray]] = []
+    for layer in range(L):
+        r = moe_layer(h, W, layer, dims)
+        layers.append(r)
+        h = r["h_out"]
+    out: Dict[str, object] = dict(h_out=h, layers=layers)
+    if lm_head:
+        out.update(lm_head_argmax(h, W["final_norm"], W["lm_head"], dims))
+    return out
+
+
+def verify_step(h_in: np.ndarray, drafts: np.ndarray, W, dims) -> Dict[str, object]:
+    """One verify step: h_in [B*(K+1), d] (row b*(K+1) is sequence b's
+    committed token, rows +1..K its drafts), drafts [B, K]."""
+    drafts = np.asarray(drafts)
+    B, K = drafts.shape
+    out = forward_tokens(h_in, W, dims)
+    g = np.asarray(out["argmax"]).reshape(B, K + 1)
+    n_acc, committed, n_committed = spec_accept(g, drafts)
+    out.update(n_accepted=n_acc, committed=committed, n_committed=n_committed)
+    return out
