@@ -27,7 +27,10 @@ a final RMSNorm precedes the LM head; argmax ties go to the lowest token id.
 
 Precision
 ---------
-All arithmetic is float64.  Values the kernel *stores* in the model's dtype
+All arithmetic is float64 (``ftype=np.float64``, the reference).  The same
+algorithm can also run with float32 working precision (``ftype=np.float32``);
+the tests use the gap between the two runs to measure how far rounding noise
+alone can move each routing and argmax decision after many layers.  Values the kernel *stores* in the model's dtype
 are rounded to it, through fp32, exactly where the kernel rounds: the hidden
 state between layers, the normalised input x of each layer, the SwiGLU
 product a, and the final normalised x_f.  Router logits and LM-head logits
@@ -96,19 +99,19 @@ def as_fp32(v: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def rms_norm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+def rms_norm(h: np.ndarray, gamma: np.ndarray, eps: float, ftype=np.float64) -> np.ndarray:
     """RMSNorm of each row: (h * (mean(h^2) + eps)^(-1/2)) * gamma."""
-    h = np.asarray(h, dtype=np.float64)
-    inv = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
-    return (h * inv) * gamma
+    h = np.asarray(h, dtype=ftype)
+    inv = ftype(1.0) / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + ftype(eps))
+    return (h * inv) * np.asarray(gamma, ftype)
 
 
 def router_logits(x: np.ndarray, w_router: np.ndarray,
-                  bias: Optional[np.ndarray]) -> np.ndarray:
+                  bias: Optional[np.ndarray], ftype=np.float64) -> np.ndarray:
     """Router logits l = x W_r^T (+ b), returned rounded to fp32."""
-    l = x @ w_router.T
+    l = np.asarray(x, ftype) @ np.asarray(w_router, ftype).T
     if bias is not None:
-        l = l + np.asarray(bias, dtype=np.float64)
+        l = l + np.asarray(bias, dtype=ftype)
     return as_fp32(l)
 
 
@@ -125,10 +128,10 @@ def select_top_k(l32: np.ndarray, k: int):
     return sel, margin
 
 
-def gate_weights(l_sel: np.ndarray) -> np.ndarray:
+def gate_weights(l_sel: np.ndarray, ftype=np.float64) -> np.ndarray:
     """Softmax over the selected logits (equal to the softmax over all experts
     renormalised to the selected ones)."""
-    l_sel = np.asarray(l_sel, dtype=np.float64)
+    l_sel = np.asarray(l_sel, dtype=ftype)
     z = np.exp(l_sel - np.max(l_sel))
     return z / np.sum(z)
 
@@ -140,19 +143,21 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def swiglu_expert(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
-                  dtype: str) -> np.ndarray:
+                  dtype: str, ftype=np.float64) -> np.ndarray:
     """One SwiGLU expert on rows x [m, d]: gate rows [0, F) and up rows [F, 2F)
     of w_gate_up [2F, d]; a = SiLU(gate) * up is stored in the model dtype;
     y = a W_down^T with w_down [d, F]."""
     F = w_gate_up.shape[0] // 2
+    x = np.asarray(x, ftype)
+    w_gate_up = np.asarray(w_gate_up, ftype)
     g = x @ w_gate_up[:F].T
     u = x @ w_gate_up[F:].T
-    a = store(silu(g) * u, dtype)
-    return a @ w_down.T
+    a = np.asarray(store(silu(g) * u, dtype), ftype)
+    return a @ np.asarray(w_down, ftype).T
 
 
 def moe_layer(h: np.ndarray, W: Dict[str, Optional[np.ndarray]], layer: int,
-              dims) -> Dict[str, np.ndarray]:
+              dims, ftype=np.float64) -> Dict[str, np.ndarray]:
     """One layer h_out = h + MoE(RMSNorm(h)) for every row of h [T, d]
     (float64 holding stored values).  Rows are independent.
 
@@ -164,9 +169,9 @@ def moe_layer(h: np.ndarray, W: Dict[str, Optional[np.ndarray]], layer: int,
     E, eps = dims.n_routed, dims.rms_eps
     T, d = h.shape
     gamma = widen(W["ffn_norm"][layer], dt)
-    x = store(rms_norm(h, gamma, eps), dt)
+    x = store(rms_norm(h, gamma, eps, ftype), dt)
     bias = None if W.get("router_b") is None else W["router_b"][layer]
-    l32 = router_logits(x, widen(W["router_w"][layer], dt), bias)
+    l32 = router_logits(x, widen(W["router_w"][layer], dt), bias, ftype)
 
     ids = np.zeros((T, k), np.int64)
     gates = np.zeros((T, k))
@@ -174,48 +179,53 @@ def moe_layer(h: np.ndarray, W: Dict[str, Optional[np.ndarray]], layer: int,
     for t in range(T):
         sel, margin[t] = select_top_k(l32[t], k)
         ids[t] = sel
-        gates[t] = gate_weights(l32[t, sel])
+        gates[t] = gate_weights(l32[t, sel], ftype)
 
     # slot[t, s] = contribution of the s-th selected expert (gate applied);
     # slots k.. are the shared experts.  Each expert runs on the rows that
     # selected it; each row is computed exactly as for a token alone.
-    slot = np.zeros((T, k + S, d))
+    slot = np.zeros((T, k + S, d), ftype)
     for e in range(E):
         rows, pos = np.nonzero(ids == e)
         if rows.size == 0:
             continue
         y_e = swiglu_expert(x[rows], widen(W["w_gate_up"][layer, e], dt),
-                            widen(W["w_down"][layer, e], dt), dt)
-        slot[rows, pos] = gates[rows, pos][:, None] * y_e
+                            widen(W["w_down"][layer, e], dt), dt, ftype)
+        slot[rows, pos] = np.asarray(gates[rows, pos], ftype)[:, None] * y_e
     for s in range(S):
         slot[:, k + s] = swiglu_expert(x, widen(W["ws_gate_up"][layer, s], dt),
-                                       widen(W["ws_down"][layer, s], dt), dt)
+                                       widen(W["ws_down"][layer, s], dt), dt, ftype)
 
-    y = np.zeros((T, d))
+    y = np.zeros((T, d), ftype)
     for s in range(k + S):          # fixed order: routed slots, then shared
         y = y + slot[:, s]
-    h_out = store(h + y, dt)
-    return dict(h_out=h_out, x=x, logits=l32, ids=ids, gates=gates, y=y,
-                margin=margin)
+    h_out = store(np.asarray(h, ftype) + y, dt)
+    return dict(h_out=h_out, x=x, logits=l32, ids=ids, gates=gates,
+                y=y.astype(np.float64), margin=margin)
 
 
 def lm_head_argmax(h: np.ndarray, final_norm: np.ndarray, lm_head: np.ndarray,
-                   dims, chunk: int = 16384) -> Dict[str, np.ndarray]:
+                   dims, chunk: int = 16384, ftype=np.float64,
+                   keep_logits: bool = False) -> Dict[str, np.ndarray]:
     """Final RMSNorm, LM-head logits z = x_f W_lm^T (fp32 for the decision),
     greedy choice g = lowest id among the maximal logits, and the margin
     between the largest and second-largest logit."""
     dt = dims.dtype
-    xf = store(rms_norm(h, widen(final_norm, dt), dims.rms_eps), dt)
+    xf = store(rms_norm(h, widen(final_norm, dt), dims.rms_eps, ftype), dt)
     V = lm_head.shape[0]
-    z = np.empty((h.shape[0], V))
+    z = np.empty((h.shape[0], V), ftype)
+    xq = np.asarray(xf, ftype)
     for v0 in range(0, V, chunk):       # the matrix is widened piecewise
-        z[:, v0:v0 + chunk] = xf @ widen(lm_head[v0:v0 + chunk], dt).T
+        z[:, v0:v0 + chunk] = xq @ np.asarray(widen(lm_head[v0:v0 + chunk], dt), ftype).T
     z32 = as_fp32(z)
     zmax = z32.max(axis=1)
     g = np.array([int(np.flatnonzero(z32[t] == zmax[t])[0]) for t in range(len(zmax))],
                  dtype=np.int64)
     top2 = np.sort(z32, axis=1)[:, -2:] if V > 1 else np.repeat(z32, 2, axis=1)
-    return dict(xf=xf, argmax=g, margin=top2[:, 1] - top2[:, 0])
+    out = dict(xf=xf, argmax=g, margin=top2[:, 1] - top2[:, 0])
+    if keep_logits:
+        out["logits"] = z32
+    return out
 
 
 def spec_accept(argmax: np.ndarray, drafts: np.ndarray):
@@ -243,19 +253,21 @@ def spec_accept(argmax: np.ndarray, drafts: np.ndarray):
 
 
 def forward_tokens(h_in: np.ndarray, W, dims, n_layers: Optional[int] = None,
-                   lm_head: bool = True) -> Dict[str, object]:
+                   lm_head: bool = True, ftype=np.float64,
+                   keep_logits: bool = False) -> Dict[str, object]:
     """The verify step's forward for any set of token rows (rows are
     independent): the MoE stack, then optionally the final norm + LM argmax."""
     L = dims.n_layers if n_layers is None else n_layers
     h = widen(h_in, dims.dtype)
     layers: List[Dict[str, np.ndarray]] = []
     for layer in range(L):
-        r = moe_layer(h, W, layer, dims)
+        r = moe_layer(h, W, layer, dims, ftype)
         layers.append(r)
         h = r["h_out"]
     out: Dict[str, object] = dict(h_out=h, layers=layers)
     if lm_head:
-        out.update(lm_head_argmax(h, W["final_norm"], W["lm_head"], dims))
+        out.update(lm_head_argmax(h, W["final_norm"], W["lm_head"], dims, ftype=ftype,
+                                  keep_logits=keep_logits))
     return out
 
 

@@ -1,0 +1,299 @@
+// C ABI of the MoE verify-step library: argument validation, workspace
+// carving and the launch sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "moe_verify.h"
+#include "mv_internal.h"
+
+#define MV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *msg) {
+  g_err = msg;
+  return code;
+}
+
+constexpr int kMaxTokens = 65535;
+constexpr int kMaxK = 15;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Layout {
+  size_t hbuf, x, ids, gates, seg, tiles, rows, a, slots, argkey, total;
+};
+
+Layout layout(const mv_config &c, int T) {
+  const size_t es = c.dtype == MV_BF16 ? 2 : 4;
+  const size_t nslot = static_cast<size_t>(c.top_k + c.n_shared);
+  const size_t ne = static_cast<size_t>(c.n_routed + c.n_shared + 1);
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.hbuf = take(static_cast<size_t>(T) * c.d_model * es);
+  L.x = take(static_cast<size_t>(T) * c.d_model * es);
+  L.ids = take(static_cast<size_t>(T) * c.top_k * 4);
+  L.gates = take(static_cast<size_t>(T) * c.top_k * 4);
+  L.seg = take(ne * 4);
+  L.tiles = take(ne * 4);
+  L.rows = take(static_cast<size_t>(T) * nslot * 4);
+  L.a = take(static_cast<size_t>(T) * nslot * c.d_ff * es);
+  L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
+  L.argkey = take(static_cast<size_t>(T) * 8);
+  L.total = off;
+  return L;
+}
+
+int check_config(const mv_config *c) {
+  if (!c) return fail(MV_ERR_NULL, "config is NULL");
+  if (c->dtype != MV_F32 && c->dtype != MV_BF16) return fail(MV_ERR_UNSUPPORTED, "dtype must be MV_F32 or MV_BF16");
+  if (c->d_model <= 0 || c->d_model % 64 || c->d_model > 4096)
+    return fail(MV_ERR_UNSUPPORTED, "d_model must be a positive multiple of 64, at most 4096");
+  if (c->d_ff <= 0 || c->d_ff % 64 || c->d_ff > 8192)
+    return fail(MV_ERR_UNSUPPORTED, "d_ff must be a positive multiple of 64, at most 8192");
+  if (c->n_routed < 1 || c->n_routed > 64) return fail(MV_ERR_UNSUPPORTED, "n_routed must be in [1, 64]");
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_routed)
+    return fail(MV_ERR_UNSUPPORTED, "top_k must be in [1, min(8, n_routed)]");
+  if (c->n_shared < 0 || c->n_shared > 4) return fail(MV_ERR_UNSUPPORTED, "n_shared must be in [0, 4]");
+  if (c->n_layers < 1) return fail(MV_ERR_UNSUPPORTED, "n_layers must be >= 1");
+  if (c->vocab < 1) return fail(MV_ERR_UNSUPPORTED, "vocab must be >= 1");
+  if (!(c->rms_eps > 0.f)) return fail(MV_ERR_UNSUPPORTED, "rms_eps must be > 0");
+  return MV_OK;
+}
+
+int check_layer_weights(const mv_config *c, const mv_weights *w) {
+  if (!w) return fail(MV_ERR_NULL, "weights is NULL");
+  if (!w->ffn_norm || !w->router_w || !w->w_gate_up || !w->w_down)
+    return fail(MV_ERR_NULL, "a layer weight pointer is NULL");
+  if (c->n_shared > 0 && (!w->ws_gate_up || !w->ws_down))
+    return fail(MV_ERR_NULL, "shared-expert weights are NULL with n_shared > 0");
+  return MV_OK;
+}
+
+int check_ws(const mv_config *c, int T, const void *ws, size_t ws_bytes) {
+  if (!ws) return fail(MV_ERR_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < layout(*c, T).total) return fail(MV_ERR_WORKSPACE, "workspace smaller than mv_workspace_bytes(cfg, T)");
+  return MV_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MV_OK;
+  g_err = std::string("HIP launch failed: ") + hipGetErrorString(e);
+  return MV_ERR_HIP;
+}
+
+// Upper bound of the number of 16-row expert tiles for T tokens.
+int max_tiles(const mv_config &c, int T) {
+  const int pairs = T * c.top_k;
+  const int busy = pairs < c.n_routed ? pairs : c.n_routed;
+  return (pairs + (mv::kTileM - 1) * busy) / mv::kTileM + c.n_shared * ((T + mv::kTileM - 1) / mv::kTileM);
+}
+
+struct LayerPtrs {
+  const void *norm, *router, *gu, *down, *sgu, *sdown;
+  const float *bias;
+};
+
+LayerPtrs layer_ptrs(const mv_config &c, const mv_weights &w, int layer) {
+  const size_t es = c.dtype == MV_BF16 ? 2 : 4;
+  const size_t d = c.d_model, F = c.d_ff, E = c.n_routed, S = c.n_shared;
+  auto at = [&](const void *base, size_t elems) {
+    return base ? static_cast<const void *>(static_cast<const char *>(base) + layer * elems * es) : nullptr;
+  };
+  LayerPtrs p;
+  p.norm = at(w.ffn_norm, d);
+  p.router = at(w.router_w, E * d);
+  p.gu = at(w.w_gate_up, E * 2 * F * d);
+  p.down = at(w.w_down, E * d * F);
+  p.sgu = at(w.ws_gate_up, S * 2 * F * d);
+  p.sdown = at(w.ws_down, S * d * F);
+  p.bias = w.router_b ? w.router_b + static_cast<size_t>(layer) * E : nullptr;
+  return p;
+}
+
+// Route (+permute), gate/up and down for one layer.  Leaves the layer's
+// expert outputs in the slot buffer; the caller's next prologue combines.
+int run_layer_experts(const mv_config &c, const LayerPtrs &lp, int T, const void *h_src, void *h_dst,
+                      const float *slots_prev, int *ids, float *gates, char *ws, const Layout &L,
+                      hipStream_t s) {
+  mv::PrologueArgs pa{};
+  pa.T = T;
+  pa.d = c.d_model;
+  pa.E = c.n_routed;
+  pa.S = c.n_shared;
+  pa.k = c.top_k;
+  pa.nslot = c.top_k + c.n_shared;
+  pa.mode = mv::kRoute;
+  pa.tile_m = mv::kTileM;
+  pa.eps = c.rms_eps;
+  pa.h_src = h_src;
+  pa.h_dst = h_dst;
+  pa.slots = slots_prev;
+  pa.gamma = lp.norm;
+  pa.x_out = ws + L.x;
+  pa.router_w = lp.router;
+  pa.router_b = lp.bias;
+  pa.ids = ids;
+  pa.gates = gates;
+  pa.seg = reinterpret_cast<int *>(ws + L.seg);
+  pa.tile_start = reinterpret_cast<int *>(ws + L.tiles);
+  pa.rows = reinterpret_cast<int *>(ws + L.rows);
+  int rc = hip_status(mv::launch_prologue(c.dtype, pa, s));
+  if (rc) return rc;
+  if ((T + mv::kPrologueTokens - 1) / mv::kPrologueTokens > 1) {
+    rc = hip_status(mv::launch_permute(pa, s));
+    if (rc) return rc;
+  }
+  mv::ExpertArgs ea{};
+  ea.T = T;
+  ea.d = c.d_model;
+  ea.F = c.d_ff;
+  ea.E = c.n_routed;
+  ea.S = c.n_shared;
+  ea.k = c.top_k;
+  ea.nslot = pa.nslot;
+  ea.x = ws + L.x;
+  ea.a = ws + L.a;
+  ea.a_out = ws + L.a;
+  ea.seg = pa.seg;
+  ea.tile_start = pa.tile_start;
+  ea.rows = pa.rows;
+  ea.gates = gates;
+  ea.slots = reinterpret_cast<float *>(ws + L.slots);
+  const int mt = max_tiles(c, T);
+  ea.w_routed = lp.gu;
+  ea.w_shared = lp.sgu;
+  rc = hip_status(mv::launch_gate_up(c.dtype, ea, mt, s));
+  if (rc) return rc;
+  ea.w_routed = lp.down;
+  ea.w_shared = lp.sdown;
+  return hip_status(mv::launch_down(c.dtype, ea, mt, s));
+}
+
+mv::PrologueArgs tail_args(const mv_config &c, int T, int mode, const void *h_src, void *h_dst,
+                           const float *slots, float *y_moe) {
+  mv::PrologueArgs pa{};
+  pa.T = T;
+  pa.d = c.d_model;
+  pa.E = c.n_routed;
+  pa.S = c.n_shared;
+  pa.k = c.top_k;
+  pa.nslot = c.top_k + c.n_shared;
+  pa.mode = mode;
+  pa.tile_m = mv::kTileM;
+  pa.eps = c.rms_eps;
+  pa.h_src = h_src;
+  pa.h_dst = h_dst;
+  pa.slots = slots;
+  pa.y_moe = y_moe;
+  return pa;
+}
+
+}  // namespace
+
+MV_API size_t mv_workspace_bytes(const mv_config *cfg, int32_t max_tokens) {
+  if (check_config(cfg) != MV_OK) return 0;
+  if (max_tokens < 0 || max_tokens > kMaxTokens) {
+    g_err = "max_tokens must be in [0, 65535]";
+    return 0;
+  }
+  return layout(*cfg, max_tokens).total;
+}
+
+MV_API int moe_layer_forward(const mv_config *cfg, const mv_weights *w, int32_t layer, int32_t T,
+                             const void *h_in, void *h_out, int32_t *topk_ids, float *topk_w,
+                             float *y_moe, void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (layer < 0 || layer >= cfg->n_layers) return fail(MV_ERR_SHAPE, "layer index out of range");
+  if (T < 0 || T > kMaxTokens) return fail(MV_ERR_SHAPE, "T must be in [0, 65535]");
+  if ((rc = check_layer_weights(cfg, w))) return rc;
+  if (T == 0) return MV_OK;
+  if (!h_in || !h_out) return fail(MV_ERR_NULL, "h_in and h_out are required");
+  if ((rc = check_ws(cfg, T, ws, ws_bytes))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(*cfg, T);
+  char *wsb = static_cast<char *>(ws);
+  int *ids = topk_ids ? topk_ids : reinterpret_cast<int *>(wsb + L.ids);
+  float *gates = topk_w ? topk_w : reinterpret_cast<float *>(wsb + L.gates);
+  const LayerPtrs lp = layer_ptrs(*cfg, *w, layer);
+  rc = run_layer_experts(*cfg, lp, T, h_in, nullptr, nullptr, ids, gates, wsb, L, s);
+  if (rc) return rc;
+  mv::PrologueArgs pa = tail_args(*cfg, T, mv::kCombine, h_in, h_out,
+                                  reinterpret_cast<const float *>(wsb + L.slots), y_moe);
+  return hip_status(mv::launch_prologue(cfg->dtype, pa, s));
+}
+
+MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
+                           const void *h_in, const int32_t *drafts, void *h_out, int32_t *argmax,
+                           int32_t *n_accepted, int32_t *committed, int32_t *n_committed,
+                           int32_t *dbg_topk_ids, void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (B < 0 || K < 0) return fail(MV_ERR_SHAPE, "B and K must be >= 0");
+  if (K > kMaxK) return fail(MV_ERR_SHAPE, "K must be at most 15");
+  const long long Tl = static_cast<long long>(B) * (K + 1);
+  if (Tl > kMaxTokens) return fail(MV_ERR_SHAPE, "B*(K+1) must be at most 65535");
+  if ((rc = check_layer_weights(cfg, w))) return rc;
+  if (!w->final_norm || !w->lm_head) return fail(MV_ERR_NULL, "final_norm and lm_head are required");
+  if (B == 0) return MV_OK;
+  const int T = static_cast<int>(Tl);
+  if (!h_in || !argmax || !n_accepted || !committed || !n_committed)
+    return fail(MV_ERR_NULL, "h_in, argmax, n_accepted, committed and n_committed are required");
+  if (K > 0 && !drafts) return fail(MV_ERR_NULL, "drafts is required when K > 0");
+  if ((rc = check_ws(cfg, T, ws, ws_bytes))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(*cfg, T);
+  char *wsb = static_cast<char *>(ws);
+  void *hbuf = h_out ? h_out : static_cast<void *>(wsb + L.hbuf);
+  const float *slots = reinterpret_cast<const float *>(wsb + L.slots);
+  for (int layer = 0; layer < cfg->n_layers; ++layer) {
+    const LayerPtrs lp = layer_ptrs(*cfg, *w, layer);
+    int *ids = dbg_topk_ids ? dbg_topk_ids + static_cast<size_t>(layer) * T * cfg->top_k
+                            : reinterpret_cast<int *>(wsb + L.ids);
+    rc = run_layer_experts(*cfg, lp, T, layer == 0 ? h_in : hbuf, hbuf, layer == 0 ? nullptr : slots,
+                           ids, reinterpret_cast<float *>(wsb + L.gates), wsb, L, s);
+    if (rc) return rc;
+  }
+  mv::PrologueArgs pa = tail_args(*cfg, T, mv::kFinal, hbuf, hbuf, slots, nullptr);
+  pa.gamma = w->final_norm;
+  pa.x_out = wsb + L.x;
+  pa.argkey = reinterpret_cast<unsigned long long *>(wsb + L.argkey);
+  if ((rc = hip_status(mv::launch_prologue(cfg->dtype, pa, s)))) return rc;
+
+  mv::LmArgs la{T, cfg->d_model, cfg->vocab, wsb + L.x, w->lm_head, pa.argkey};
+  if ((rc = hip_status(mv::launch_lm_argmax(cfg->dtype, la, s)))) return rc;
+
+  mv::AcceptArgs aa{B, K, pa.argkey, nullptr, argmax, drafts, n_accepted, committed, n_committed};
+  return hip_status(mv::launch_accept(aa, s));
+}
+
+MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_t *drafts,
+                       int32_t *n_accepted, int32_t *committed, int32_t *n_committed, void *stream) {
+  g_err.clear();
+  if (B < 0 || K < 0) return fail(MV_ERR_SHAPE, "B and K must be >= 0");
+  if (K > kMaxK) return fail(MV_ERR_SHAPE, "K must be at most 15");
+  if (B == 0) return MV_OK;
+  if (!argmax || !n_accepted || !committed || !n_committed)
+    return fail(MV_ERR_NULL, "argmax, n_accepted, committed and n_committed are required");
+  if (K > 0 && !drafts) return fail(MV_ERR_NULL, "drafts is required when K > 0");
+  mv::AcceptArgs aa{B, K, nullptr, argmax, nullptr, drafts, n_accepted, committed, n_committed};
+  return hip_status(mv::launch_accept(aa, static_cast<hipStream_t>(stream)));
+}
+
+MV_API const char *mv_last_error(void) { return g_err.c_str(); }

@@ -187,14 +187,18 @@ def make_weights(dims: ModelDims, seed: int = 0, sigma: Optional[float] = None,
     else:
         raise ValueError(gamma)
 
-    w["router_b"] = None
-    if zipf_s is not None:
-        b = np.empty((L, E), np.float32)
-        for layer in range(L):
-            rank = _rng(seed, _K_PERM, layer).permutation(E) + 1
-            b[layer] = (-zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
-        w["router_b"] = b
+    w["router_b"] = None if zipf_s is None else make_router_bias(L, E, zipf_s, seed)
     return w
+
+
+def make_router_bias(n_layers: int, n_routed: int, zipf_s: float, seed: int = 0) -> np.ndarray:
+    """Router bias [L, E] fp32 skewing expert popularity: b_e = -s * ln(rank_e)
+    over a seeded random ranking of the experts in each layer."""
+    b = np.empty((n_layers, n_routed), np.float32)
+    for layer in range(n_layers):
+        rank = _rng(seed, _K_PERM, layer).permutation(n_routed) + 1
+        b[layer] = (-zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
+    return b
 
 
 def workload_weights(wl: Workload, seed: int = 0, **kw):

@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments before it
+enqueues anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decode_verification_router_amd import binding as bd
+from speculative_decode_verification_router_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+
+def header_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_]\w*\s*\**\s*([A-Za-z_]\w*)\s*\(", text, re.M)
+    return sorted(set(names) - {"if", "while", "for", "return"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from speculative_decode_verification_router_amd import build
+
+        build.build()
+    return bd.load()
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(bd.EXPORTED)
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def _cfg(dims=synth.DS3B_BF16, **kw):
+    c = bd.make_config(dims)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_bytes(lib):
+    c = _cfg()
+    w4, w128 = bd.mv_workspace_bytes(c, 4), bd.mv_workspace_bytes(c, 128)
+    assert 0 < w4 < w128
+    assert w4 % 256 == 0
+    # dominant terms: fp32 slot buffer and bf16 SwiGLU rows, 8 slots per token
+    assert w128 >= 128 * 8 * (1280 * 4 + 896 * 2)
+    assert bd.mv_workspace_bytes(c, 0) > 0
+    assert bd.mv_workspace_bytes(c, -1) == 0
+    assert bd.mv_workspace_bytes(c, 65536) == 0
+    assert bd.mv_workspace_bytes(_cfg(d_model=1000), 4) == 0
+    assert bd.mv_workspace_bytes(_cfg(dtype=7), 4) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation or is a no-op
+
+
+def _weights(**kw):
+    w = bd.MvWeights(*([FAKE] * 9))
+    w.router_b = None
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def _verify(lib, cfg, w, B=1, K=3, h_in=FAKE, drafts=FAKE, argmax=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.moe_verify_step(ctypes.byref(cfg) if cfg is not None else None,
+                               ctypes.byref(w) if w is not None else None, B, K, h_in, drafts,
+                               None, argmax, FAKE, FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(cfg=None), bd.MV_ERR_NULL),
+    (dict(w=None), bd.MV_ERR_NULL),
+    (dict(h_in=None), bd.MV_ERR_NULL),
+    (dict(argmax=None), bd.MV_ERR_NULL),
+    (dict(drafts=None), bd.MV_ERR_NULL),
+    (dict(ws=None), bd.MV_ERR_NULL),
+    (dict(B=-1), bd.MV_ERR_SHAPE),
+    (dict(K=-1), bd.MV_ERR_SHAPE),
+    (dict(K=16), bd.MV_ERR_SHAPE),
+    (dict(B=20000, K=3), bd.MV_ERR_SHAPE),
+    (dict(ws_bytes=1024), bd.MV_ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), bd.MV_ERR_WORKSPACE),
+    (dict(cfg_kw=dict(dtype=3)), bd.MV_ERR_UNSUPPORTED),
+    (dict(cfg_kw=dict(top_k=9)), bd.MV_ERR_UNSUPPORTED),
+    (dict(cfg_kw=dict(n_routed=65)), bd.MV_ERR_UNSUPPORTED),
+    (dict(cfg_kw=dict(d_model=1300)), bd.MV_ERR_UNSUPPORTED),
+    (dict(cfg_kw=dict(d_ff=100)), bd.MV_ERR_UNSUPPORTED),
+    (dict(cfg_kw=dict(rms_eps=0.0)), bd.MV_ERR_UNSUPPORTED),
+    (dict(w_kw=dict(lm_head=None)), bd.MV_ERR_NULL),
+    (dict(w_kw=dict(ws_down=None)), bd.MV_ERR_NULL),
+])
+def test_verify_step_rejects_bad_arguments(lib, case, code):
+    case = dict(case)
+    cfg = _cfg(**case.pop("cfg_kw", {})) if "cfg" not in case else case.pop("cfg")
+    w = _weights(**case.pop("w_kw", {})) if "w" not in case else case.pop("w")
+    assert _verify(lib, cfg, w, **case) == code
+    assert bd.mv_last_error() != ""
+
+
+def test_zero_sequences_is_a_no_op(lib):
+    assert _verify(lib, _cfg(), _weights(), B=0, h_in=None, argmax=None, ws=None) == bd.MV_OK
+    assert bd.mv_last_error() == ""
+
+
+def test_layer_forward_rejects_bad_arguments(lib):
+    cfg, w = _cfg(), _weights()
+    call = lambda layer, T, h_in=FAKE, ws=FAKE, ws_bytes=1 << 40: lib.moe_layer_forward(
+        ctypes.byref(cfg), ctypes.byref(w), layer, T, h_in, FAKE, None, None, None, ws, ws_bytes, None)
+    assert call(12, 4) == bd.MV_ERR_SHAPE
+    assert call(-1, 4) == bd.MV_ERR_SHAPE
+    assert call(0, -1) == bd.MV_ERR_SHAPE
+    assert call(0, 4, h_in=None) == bd.MV_ERR_NULL
+    assert call(0, 4, ws_bytes=10) == bd.MV_ERR_WORKSPACE
+    assert call(0, 0, h_in=None, ws=None) == bd.MV_OK
+
+
+def test_spec_accept_rejects_bad_arguments(lib):
+    assert lib.spec_accept(-1, 3, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MV_ERR_SHAPE
+    assert lib.spec_accept(1, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.MV_ERR_SHAPE
+    assert lib.spec_accept(1, 3, None, FAKE, FAKE, FAKE, FAKE, None) == bd.MV_ERR_NULL
+    assert lib.spec_accept(1, 3, FAKE, None, FAKE, FAKE, FAKE, None) == bd.MV_ERR_NULL
+    assert lib.spec_accept(0, 3, None, None, None, None, None, None) == bd.MV_OK
