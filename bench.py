@@ -51,6 +51,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-baseline-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time graph replays")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -87,20 +89,35 @@ def main(argv=None):
     drafts = bd.to_device(drafts_np)
 
     out = bd.run_verify_step(model, h, drafts, B, K)
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+
+    def step(stream):
         bd.moe_verify_step(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
                            out["n_accepted"], out["committed"], out["n_committed"], None,
                            model.ws, model.ws_bytes, stream)
+
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                step(side)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream())
+        run = lambda stream: graph.replay()  # noqa: E731
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        run(stream)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        bd.moe_verify_step(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
-                           out["n_accepted"], out["committed"], out["n_committed"], None,
-                           model.ws, model.ws_bytes, stream)
+        run(stream)
+    t_enq = time.perf_counter() - t0
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -135,6 +152,8 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 4),
+        "host_enqueue_ms_per_step": round(t_enq / args.steps * 1e3, 4),
+        "graph": bool(args.graph),
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -25,8 +25,15 @@ constexpr int kMaxK = 15;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Upper bound of the number of 16-row expert tiles for T tokens.
+int max_tiles(const mv_config &c, int T) {
+  const int pairs = T * c.top_k;
+  const int busy = pairs < c.n_routed ? pairs : c.n_routed;
+  return (pairs + (mv::kTileM - 1) * busy) / mv::kTileM + c.n_shared * ((T + mv::kTileM - 1) / mv::kTileM);
+}
+
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, rows, a, slots, argkey, total;
+  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -46,6 +53,7 @@ Layout layout(const mv_config &c, int T) {
   L.gates = take(static_cast<size_t>(T) * c.top_k * 4);
   L.seg = take(ne * 4);
   L.tiles = take(ne * 4);
+  L.tinfo = take(static_cast<size_t>(max_tiles(c, T)) * 16);
   L.rows = take(static_cast<size_t>(T) * nslot * 4);
   L.a = take(static_cast<size_t>(T) * nslot * c.d_ff * es);
   L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
@@ -93,13 +101,6 @@ int hip_status(hipError_t e) {
   return MV_ERR_HIP;
 }
 
-// Upper bound of the number of 16-row expert tiles for T tokens.
-int max_tiles(const mv_config &c, int T) {
-  const int pairs = T * c.top_k;
-  const int busy = pairs < c.n_routed ? pairs : c.n_routed;
-  return (pairs + (mv::kTileM - 1) * busy) / mv::kTileM + c.n_shared * ((T + mv::kTileM - 1) / mv::kTileM);
-}
-
 struct LayerPtrs {
   const void *norm, *router, *gu, *down, *sgu, *sdown;
   const float *bias;
@@ -122,83 +123,100 @@ LayerPtrs layer_ptrs(const mv_config &c, const mv_weights &w, int layer) {
   return p;
 }
 
-// Route (+permute), gate/up and down for one layer.  Leaves the layer's
-// expert outputs in the slot buffer; the caller's next prologue combines.
-int run_layer_experts(const mv_config &c, const LayerPtrs &lp, int T, const void *h_src, void *h_dst,
-                      const float *slots_prev, int *ids, float *gates, char *ws, const Layout &L,
-                      hipStream_t s) {
-  mv::PrologueArgs pa{};
-  pa.T = T;
-  pa.d = c.d_model;
-  pa.E = c.n_routed;
-  pa.S = c.n_shared;
-  pa.k = c.top_k;
-  pa.nslot = c.top_k + c.n_shared;
-  pa.mode = mv::kRoute;
-  pa.tile_m = mv::kTileM;
-  pa.eps = c.rms_eps;
-  pa.h_src = h_src;
-  pa.h_dst = h_dst;
-  pa.slots = slots_prev;
-  pa.gamma = lp.norm;
-  pa.x_out = ws + L.x;
-  pa.router_w = lp.router;
-  pa.router_b = lp.bias;
-  pa.ids = ids;
-  pa.gates = gates;
-  pa.seg = reinterpret_cast<int *>(ws + L.seg);
-  pa.tile_start = reinterpret_cast<int *>(ws + L.tiles);
-  pa.rows = reinterpret_cast<int *>(ws + L.rows);
-  int rc = hip_status(mv::launch_prologue(c.dtype, pa, s));
-  if (rc) return rc;
-  if ((T + mv::kPrologueTokens - 1) / mv::kPrologueTokens > 1) {
-    rc = hip_status(mv::launch_permute(pa, s));
-    if (rc) return rc;
-  }
-  mv::ExpertArgs ea{};
-  ea.T = T;
-  ea.d = c.d_model;
-  ea.F = c.d_ff;
-  ea.E = c.n_routed;
-  ea.S = c.n_shared;
-  ea.k = c.top_k;
-  ea.nslot = pa.nslot;
-  ea.x = ws + L.x;
-  ea.a = ws + L.a;
-  ea.a_out = ws + L.a;
-  ea.seg = pa.seg;
-  ea.tile_start = pa.tile_start;
-  ea.rows = pa.rows;
-  ea.gates = gates;
-  ea.slots = reinterpret_cast<float *>(ws + L.slots);
-  const int mt = max_tiles(c, T);
-  ea.w_routed = lp.gu;
-  ea.w_shared = lp.sgu;
-  rc = hip_status(mv::launch_gate_up(c.dtype, ea, mt, s));
-  if (rc) return rc;
-  ea.w_routed = lp.down;
-  ea.w_shared = lp.sdown;
-  return hip_status(mv::launch_down(c.dtype, ea, mt, s));
-}
+struct Step {
+  const mv_config &c;
+  const mv_weights &w;
+  int T;
+  char *ws;
+  Layout L;
+  hipStream_t s;
 
-mv::PrologueArgs tail_args(const mv_config &c, int T, int mode, const void *h_src, void *h_dst,
-                           const float *slots, float *y_moe) {
-  mv::PrologueArgs pa{};
-  pa.T = T;
-  pa.d = c.d_model;
-  pa.E = c.n_routed;
-  pa.S = c.n_shared;
-  pa.k = c.top_k;
-  pa.nslot = c.top_k + c.n_shared;
-  pa.mode = mode;
-  pa.tile_m = mv::kTileM;
-  pa.eps = c.rms_eps;
-  pa.h_src = h_src;
-  pa.h_dst = h_dst;
-  pa.slots = slots;
-  pa.y_moe = y_moe;
-  return pa;
-}
+  int *seg() const { return reinterpret_cast<int *>(ws + L.seg); }
+  int *tiles() const { return reinterpret_cast<int *>(ws + L.tiles); }
+  int *rows() const { return reinterpret_cast<int *>(ws + L.rows); }
+  int4 *tinfo() const { return reinterpret_cast<int4 *>(ws + L.tinfo); }
+  float *slots() const { return reinterpret_cast<float *>(ws + L.slots); }
+  float *gates() const { return reinterpret_cast<float *>(ws + L.gates); }
+  unsigned long long *argkey() const { return reinterpret_cast<unsigned long long *>(ws + L.argkey); }
+
+  mv::RouteArgs route_args(int layer, int mode, int *ids, float *gates_out) const {
+    mv::RouteArgs a{};
+    a.T = T;
+    a.d = c.d_model;
+    a.E = c.n_routed;
+    a.S = c.n_shared;
+    a.k = c.top_k;
+    a.nslot = c.top_k + c.n_shared;
+    a.mode = mode;
+    a.eps = c.rms_eps;
+    a.x_out = ws + L.x;
+    a.seg = seg();
+    a.tile_start = tiles();
+    a.rows = rows();
+    a.tile_info = tinfo();
+    a.ids = ids;
+    a.gates = gates_out;
+    if (mode == mv::kFinal) {
+      a.gamma = w.final_norm;
+      a.argkey = argkey();
+    } else if (mode == mv::kRoute) {
+      const LayerPtrs lp = layer_ptrs(c, w, layer);
+      a.gamma = lp.norm;
+      a.router_w = lp.router;
+      a.router_b = lp.bias;
+    }
+    return a;
+  }
+
+  bool small() const { return T <= mv::kSmallT; }
+
+  // One routing launch (+ the grouping kernel on the large-batch path).
+  // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
+  int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
+            float *y_moe, int *ids, float *gates_out) const {
+    const mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
+    mv::CombineArgs cb{};
+    cb.h_src = h_src;
+    cb.h_dst = h_dst;
+    cb.slots = slots_in;
+    cb.y_moe = y_moe;
+    int rc = hip_status(mv::launch_route(c.dtype, a, cb, small() ? 1 : mv::kTileM, s));
+    if (rc || mode != mv::kRoute || small()) return rc;
+    return hip_status(mv::launch_permute(a, s));
+  }
+
+  // gate/up then down for `layer`, leaving the weighted expert outputs in slots.
+  int ffn(int layer, const int *ids_in, const float *gates_in) const {
+    const LayerPtrs lp = layer_ptrs(c, w, layer);
+    mv::ExpertArgs e{};
+    e.T = T;
+    e.d = c.d_model;
+    e.F = c.d_ff;
+    e.E = c.n_routed;
+    e.S = c.n_shared;
+    e.k = c.top_k;
+    e.nslot = c.top_k + c.n_shared;
+    e.x = ws + L.x;
+    e.a = ws + L.a;
+    e.a_out = ws + L.a;
+    e.seg = seg();
+    e.tile_start = tiles();
+    e.rows = rows();
+    e.tile_info = tinfo();
+    e.ids = ids_in;
+    e.group_in_block = small() ? 1 : 0;
+    e.gates = gates_in;
+    e.slots = slots();
+    const int mt = max_tiles(c, T);
+    e.w_routed = lp.gu;
+    e.w_shared = lp.sgu;
+    int rc = hip_status(mv::launch_gate_up(c.dtype, e, mt, s));
+    if (rc) return rc;
+    e.w_routed = lp.down;
+    e.w_shared = lp.sdown;
+    return hip_status(mv::launch_down(c.dtype, e, mt, s));
+  }
+};
 
 }  // namespace
 
@@ -224,17 +242,12 @@ MV_API int moe_layer_forward(const mv_config *cfg, const mv_weights *w, int32_t 
   if (!h_in || !h_out) return fail(MV_ERR_NULL, "h_in and h_out are required");
   if ((rc = check_ws(cfg, T, ws, ws_bytes))) return rc;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Layout L = layout(*cfg, T);
-  char *wsb = static_cast<char *>(ws);
-  int *ids = topk_ids ? topk_ids : reinterpret_cast<int *>(wsb + L.ids);
-  float *gates = topk_w ? topk_w : reinterpret_cast<float *>(wsb + L.gates);
-  const LayerPtrs lp = layer_ptrs(*cfg, *w, layer);
-  rc = run_layer_experts(*cfg, lp, T, h_in, nullptr, nullptr, ids, gates, wsb, L, s);
-  if (rc) return rc;
-  mv::PrologueArgs pa = tail_args(*cfg, T, mv::kCombine, h_in, h_out,
-                                  reinterpret_cast<const float *>(wsb + L.slots), y_moe);
-  return hip_status(mv::launch_prologue(cfg->dtype, pa, s));
+  Step st{*cfg, *w, T, static_cast<char *>(ws), layout(*cfg, T), static_cast<hipStream_t>(stream)};
+  int *ids = topk_ids ? topk_ids : reinterpret_cast<int *>(st.ws + st.L.ids);
+  float *gates = topk_w ? topk_w : st.gates();
+  if ((rc = st.route(layer, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates))) return rc;
+  if ((rc = st.ffn(layer, ids, gates))) return rc;
+  return st.route(layer, mv::kCombine, h_in, h_out, st.slots(), y_moe, nullptr, nullptr);
 }
 
 MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
@@ -257,30 +270,29 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
   if (K > 0 && !drafts) return fail(MV_ERR_NULL, "drafts is required when K > 0");
   if ((rc = check_ws(cfg, T, ws, ws_bytes))) return rc;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Layout L = layout(*cfg, T);
-  char *wsb = static_cast<char *>(ws);
-  void *hbuf = h_out ? h_out : static_cast<void *>(wsb + L.hbuf);
-  const float *slots = reinterpret_cast<const float *>(wsb + L.slots);
-  for (int layer = 0; layer < cfg->n_layers; ++layer) {
-    const LayerPtrs lp = layer_ptrs(*cfg, *w, layer);
-    int *ids = dbg_topk_ids ? dbg_topk_ids + static_cast<size_t>(layer) * T * cfg->top_k
-                            : reinterpret_cast<int *>(wsb + L.ids);
-    rc = run_layer_experts(*cfg, lp, T, layer == 0 ? h_in : hbuf, hbuf, layer == 0 ? nullptr : slots,
-                           ids, reinterpret_cast<float *>(wsb + L.gates), wsb, L, s);
-    if (rc) return rc;
+  Step st{*cfg, *w, T, static_cast<char *>(ws), layout(*cfg, T), static_cast<hipStream_t>(stream)};
+  void *hbuf = h_out ? h_out : static_cast<void *>(st.ws + st.L.hbuf);
+  const int L = cfg->n_layers, k = cfg->top_k;
+  float *gates = st.gates();
+  for (int layer = 0; layer < L; ++layer) {
+    int *ids = dbg_topk_ids ? dbg_topk_ids + static_cast<size_t>(layer) * T * k
+                            : reinterpret_cast<int *>(st.ws + st.L.ids);
+    // layer 0 routes h_in; later layers first add the previous layer's experts
+    if (layer == 0)
+      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates);
+    else
+      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates);
+    if (rc || (rc = st.ffn(layer, ids, gates))) return rc;
   }
-  mv::PrologueArgs pa = tail_args(*cfg, T, mv::kFinal, hbuf, hbuf, slots, nullptr);
-  pa.gamma = w->final_norm;
-  pa.x_out = wsb + L.x;
-  pa.argkey = reinterpret_cast<unsigned long long *>(wsb + L.argkey);
-  if ((rc = hip_status(mv::launch_prologue(cfg->dtype, pa, s)))) return rc;
+  if ((rc = st.route(L - 1, mv::kFinal, L == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, nullptr,
+                     nullptr)))
+    return rc;
 
-  mv::LmArgs la{T, cfg->d_model, cfg->vocab, wsb + L.x, w->lm_head, pa.argkey};
-  if ((rc = hip_status(mv::launch_lm_argmax(cfg->dtype, la, s)))) return rc;
+  mv::LmArgs la{T, cfg->d_model, cfg->vocab, st.ws + st.L.x, w->lm_head, st.argkey()};
+  if ((rc = hip_status(mv::launch_lm_argmax(cfg->dtype, la, st.s)))) return rc;
 
-  mv::AcceptArgs aa{B, K, pa.argkey, nullptr, argmax, drafts, n_accepted, committed, n_committed};
-  return hip_status(mv::launch_accept(aa, s));
+  mv::AcceptArgs aa{B, K, st.argkey(), nullptr, argmax, drafts, n_accepted, committed, n_committed};
+  return hip_status(mv::launch_accept(aa, st.s));
 }
 
 MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_t *drafts,

@@ -1,175 +1,216 @@
 // Grouped expert FFN kernels (routed experts and the always-on shared ones).
 //
-// Both kernels work on "tiles" of up to 16 rows of one expert's segment of
-// the sorted (token, slot) pair list.  The A operand (activation rows) is
-// staged in LDS; the weights are streamed from HBM once per tile straight
-// into MFMA operand registers (16-byte loads, several K-windows in flight per
-// lane).  Each wavefront owns 16 output columns over the full K.
+// Work is organised in tiles of up to 16 rows of one expert's segment of the
+// sorted (token, slot) pair list.  A block stages its tile's activation rows
+// in LDS (the MFMA A operand) and streams weight rows from HBM straight into
+// MFMA B-operand registers with 16-byte loads, eight K-windows in flight per
+// wavefront.
 //
-//   gate/up:  g = x W_gate^T, u = x W_up^T (fp32), a = round(SiLU(g) * u)
-//   down:     y = a W_down^T (fp32); slot[pair] = w_pair * y
-// where w_pair is the softmax gate of the routed pair, or 1 for a shared
-// expert (architecture paragraph of "Jina AI Releases jina-ocr-v1, a 3.4B
-// MoE Document Parser With Built-In Speculative Decoding", ainewsfeed.tech:
-// two shared experts beside 64 routed ones).
-#include "mv_common.h"
-#include "mv_internal.h"
+//   gate/up:  block = two 16-column slices of F; per slice one wavefront
+//             streams the gate rows and one the up rows over the full K = d;
+//             a = round(SiLU(g) * u) after an LDS exchange.
+//   down:     block = two 16-column slices of d; per slice two wavefronts
+//             split K = F in halves, added in a fixed order through LDS;
+//             slot[pair] = w_pair * y.
+// w_pair is the softmax gate of the routed pair, or 1 for a shared expert
+// (architecture paragraph of "Jina AI Releases jina-ocr-v1, a 3.4B MoE
+// Document Parser With Built-In Speculative Decoding", ainewsfeed.tech: two
+// shared experts beside 64 routed ones).
+//
+// Small batches skip the separate grouping kernel: every gate/up block groups
+// the T*k routed pairs itself (one wavefront, a few ballots per expert) and
+// block (0, 0) also writes the grouping for the down kernel.
+#include "route_core.h"
 
 namespace mv {
 
 namespace {
 
-constexpr int kWaves = 4;   // wavefronts per block, 16 columns each
-constexpr int kUnroll = 8;  // K-windows whose loads are issued together
+constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kUnroll = 8;     // K-windows whose loads are issued together
 
 struct TileInfo {
   int e, r0, m;
 };
 
-__device__ __forceinline__ bool find_tile(const ExpertArgs &p, int tile, TileInfo &ti) {
+template <typename T>
+__device__ __forceinline__ const T *expert_base(const ExpertArgs &p, int e, size_t elems) {
+  return e < p.E ? static_cast<const T *>(p.w_routed) + static_cast<size_t>(e) * elems
+                 : static_cast<const T *>(p.w_shared) + static_cast<size_t>(e - p.E) * elems;
+}
+
+// Weight loads of windows [w0, min(w0 + kUnroll, w_hi)) into registers.
+template <typename T>
+__device__ __forceinline__ void load_batch(uint4 *q, const T *b, int w0, int w_hi) {
+  constexpr int W = 4 * Vec<T>::N;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (w0 + u < w_hi) q[u] = ld16(b + (w0 + u) * W);
+}
+
+// acc += A[16 x K] * B[K x 16] over windows [w_lo, w_hi), the first batch of
+// weights already in `q`: lane l reads A row (l % 16) from `a` (LDS) and B
+// column (l % 16) from `b` (global), both at K offset (l / 16) * VN inside
+// each window of 4*VN elements.
+template <typename T>
+__device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
+                                           uint4 *q) {
+  constexpr int W = 4 * Vec<T>::N;
+  for (int w0 = w_lo; w0 < w_hi; w0 += kUnroll) {
+    if (w0 != w_lo) load_batch<T>(q, b, w0, w_hi);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+  }
+}
+
+// Grouping of a small batch, built in LDS by every gate/up block.
+struct Grouping {
+  int seg[kMaxExperts + 1];
+  int tile_start[kMaxExperts + 1];
+  int rows[kSmallT * kMaxSlots];
+};
+
+// Tile `tile` of the grouping: from the global table (large batches) or,
+// for small batches, by grouping the pairs in this block.
+__device__ bool block_tile(const ExpertArgs &p, int tile, TileInfo &ti, Grouping &g, bool write_global) {
   const int ne = p.E + p.S;
-  if (tile >= p.tile_start[ne]) return false;
+  if (!p.group_in_block) {
+    if (tile >= p.tile_start[ne]) return false;
+    const int4 v = p.tile_info[tile];
+    ti.e = v.x;
+    ti.r0 = v.y;
+    ti.m = v.z;
+    return true;
+  }
+  const GroupOut lds{g.seg, g.tile_start, g.rows, nullptr};
+  group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds);
+  __syncthreads();
+  if (write_global) {  // the grouping of record, for the down kernel
+    for (int i = threadIdx.x; i <= ne; i += blockDim.x) {
+      p.seg[i] = g.seg[i];
+      p.tile_start[i] = g.tile_start[i];
+    }
+    for (int i = threadIdx.x; i < p.T * p.nslot; i += blockDim.x) p.rows[i] = g.rows[i];
+    for (int e = threadIdx.x; e < ne; e += blockDim.x) {
+      const int c = g.seg[e + 1] - g.seg[e];
+      for (int j = 0; j * kTileM < c; ++j)
+        p.tile_info[g.tile_start[e] + j] =
+            make_int4(e, g.seg[e] + j * kTileM, min(kTileM, c - j * kTileM), 0);
+    }
+  }
+  if (tile >= g.tile_start[ne]) return false;
   int e = 0;
-  while (e + 1 < ne && p.tile_start[e + 1] <= tile) ++e;
+  while (e + 1 < ne && g.tile_start[e + 1] <= tile) ++e;
   ti.e = e;
-  ti.r0 = p.seg[e] + (tile - p.tile_start[e]) * kTileM;
-  ti.m = min(kTileM, p.seg[e + 1] - ti.r0);
+  ti.r0 = g.seg[e] + (tile - g.tile_start[e]) * kTileM;
+  ti.m = min(kTileM, g.seg[e + 1] - ti.r0);
   return true;
 }
 
-// acc += A[16 x K] * B[K x 16] where lane l reads A row (l % 16) from `a`
-// (LDS) and B column (l % 16) from `b` (global), both at K offset
-// (l / 16) * VN inside each window of 4*VN elements.
 template <typename T>
-__device__ __forceinline__ void mfma_rowpanel(f32x4_t &acc, const T *a, const T *b, int nwin) {
-  constexpr int W = 4 * Vec<T>::N;
-  for (int w0 = 0; w0 < nwin; w0 += kUnroll) {
-    uint4 bq[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (w0 + u < nwin) bq[u] = ld16(b + (w0 + u) * W);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (w0 + u < nwin) mfma16(acc, ld16(a + (w0 + u) * W), bq[u], T());
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void mfma_rowpanel2(f32x4_t &acc0, f32x4_t &acc1, const T *a,
-                                               const T *b0, const T *b1, int nwin) {
-  constexpr int W = 4 * Vec<T>::N;
-  for (int w0 = 0; w0 < nwin; w0 += kUnroll) {
-    uint4 q0[kUnroll], q1[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (w0 + u < nwin) {
-        q0[u] = ld16(b0 + (w0 + u) * W);
-        q1[u] = ld16(b1 + (w0 + u) * W);
-      }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (w0 + u < nwin) {
-        const uint4 av = ld16(a + (w0 + u) * W);
-        mfma16(acc0, av, q0[u], T());
-        mfma16(acc1, av, q1[u], T());
-      }
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_gate_up(ExpertArgs p) {
+__global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ Grouping g;
+  __shared__ float up_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
   TileInfo ti;
-  if (!find_tile(p, blockIdx.y, ti)) return;
+  if (!block_tile(p, blockIdx.y, ti, g, p.group_in_block && blockIdx.x == 0 && blockIdx.y == 0))
+    return;
   const int d = p.d, F = p.F, nvec = d / VN, lda = d + VN;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slice = wv >> 1, which = wv & 1;  // which: 0 gate rows, 1 up rows
+  const int f0 = (blockIdx.x * 2 + slice) * 16;
+  const int r = lane & 15, koff = (lane >> 4) * VN;
+  const int nwin = f0 < F ? d / (4 * VN) : 0;
+  const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(2) * F * d);
+  const T *b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
+  uint4 q[kUnroll];
+  load_batch<T>(q, b, 0, nwin);  // first weights in flight while x is staged
+
+  const int *rows = p.group_in_block ? g.rows : p.rows;
   T *A = reinterpret_cast<T *>(smem);
   const T *x = static_cast<const T *>(p.x);
-  for (int i = threadIdx.x; i < kTileM * nvec; i += blockDim.x) {
-    const int r = i / nvec, c = i - r * nvec;
+  for (int it = threadIdx.x; it < kTileM * nvec; it += blockDim.x) {
+    const int rr = it / nvec, c = it - rr * nvec;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < ti.m) {
-      const int tok = p.rows[ti.r0 + r] / p.nslot;
-      v = ld16(x + static_cast<size_t>(tok) * d + c * VN);
-    }
-    st16(A + r * lda + c * VN, v);
+    if (rr < ti.m) v = ld16(x + static_cast<size_t>(rows[ti.r0 + rr] / p.nslot) * d + c * VN);
+    st16(A + rr * lda + c * VN, v);
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int f0 = (blockIdx.x * kWaves + wv) * 16;
-  if (f0 >= F) return;
-  const size_t expert_elems = static_cast<size_t>(2) * F * d;
-  const T *W = ti.e < p.E
-                   ? static_cast<const T *>(p.w_routed) + static_cast<size_t>(ti.e) * expert_elems
-                   : static_cast<const T *>(p.w_shared) + static_cast<size_t>(ti.e - p.E) * expert_elems;
-  const int koff = (lane >> 4) * VN;
-  const T *bg = W + static_cast<size_t>(f0 + (lane & 15)) * d + koff;
-  const T *bu = bg + static_cast<size_t>(F) * d;
-  const T *ar = A + (lane & 15) * lda + koff;
-
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  mfma_rowpanel2<T>(accg, accu, ar, bg, bu, d / (4 * VN));
-
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  mfma_panel<T>(acc, A + r * lda + koff, b, 0, nwin, q);
+  if (which == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) up_acc[slice][lane][i] = acc[i];
+  }
+  __syncthreads();
+  if (which == 1 || f0 >= F) return;
   T *aout = static_cast<T *>(p.a_out);
-  const int col = f0 + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (lane >> 4) * 4 + i;
-    if (r < ti.m) {
-      const float g = accg[i], u = accu[i];
-      aout[static_cast<size_t>(ti.r0 + r) * F + col] = from_f32<T>(g / (1.0f + expf(-g)) * u);
+    const int row = (lane >> 4) * 4 + i;
+    if (row < ti.m) {
+      const float gv = acc[i], uv = up_acc[slice][lane][i];
+      aout[static_cast<size_t>(ti.r0 + row) * F + f0 + r] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
     }
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_down(ExpertArgs p) {
+__global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float half_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
-  TileInfo ti;
-  if (!find_tile(p, blockIdx.y, ti)) return;
+  if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
+  const int4 tv = p.tile_info[blockIdx.y];
+  const TileInfo ti{tv.x, tv.y, tv.z};
   const int d = p.d, F = p.F, nvec = F / VN, lda = F + VN;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slice = wv >> 1, half = wv & 1;
+  const int n0 = (blockIdx.x * 2 + slice) * 16;
+  const int r = lane & 15, koff = (lane >> 4) * VN;
+  const int nwin = F / (4 * VN);
+  const int w_lo = n0 < d ? half * nwin / 2 : 0, w_hi = n0 < d ? (half + 1) * nwin / 2 : 0;
+  const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
+  const T *b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
+  uint4 q[kUnroll];
+  load_batch<T>(q, b, w_lo, w_hi);  // first weights in flight while a is staged
+
   T *A = reinterpret_cast<T *>(smem);
   const T *a = static_cast<const T *>(p.a);
-  for (int i = threadIdx.x; i < kTileM * nvec; i += blockDim.x) {
-    const int r = i / nvec, c = i - r * nvec;
+  for (int it = threadIdx.x; it < kTileM * nvec; it += blockDim.x) {
+    const int rr = it / nvec, c = it - rr * nvec;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < ti.m) v = ld16(a + static_cast<size_t>(ti.r0 + r) * F + c * VN);
-    st16(A + r * lda + c * VN, v);
+    if (rr < ti.m) v = ld16(a + static_cast<size_t>(ti.r0 + rr) * F + c * VN);
+    st16(A + rr * lda + c * VN, v);
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * kWaves + wv) * 16;
-  if (n0 >= d) return;
-  const size_t expert_elems = static_cast<size_t>(d) * F;
-  const T *W = ti.e < p.E
-                   ? static_cast<const T *>(p.w_routed) + static_cast<size_t>(ti.e) * expert_elems
-                   : static_cast<const T *>(p.w_shared) + static_cast<size_t>(ti.e - p.E) * expert_elems;
-  const int koff = (lane >> 4) * VN;
-  const T *b = W + static_cast<size_t>(n0 + (lane & 15)) * F + koff;
-  const T *ar = A + (lane & 15) * lda + koff;
-
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  mfma_rowpanel<T>(acc, ar, b, F / (4 * VN));
-
-  const int col = n0 + (lane & 15);
+  mfma_panel<T>(acc, A + r * lda + koff, b, w_lo, w_hi, q);
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) half_acc[slice][lane][i] = acc[i];
+  }
+  __syncthreads();
+  if (half == 1 || n0 >= d) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (lane >> 4) * 4 + i;
-    if (r < ti.m) {
-      const int pair = p.rows[ti.r0 + r];
+    const int row = (lane >> 4) * 4 + i;
+    if (row < ti.m) {
+      const int pair = p.rows[ti.r0 + row];
       const int tok = pair / p.nslot, s = pair - tok * p.nslot;
       const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
-      p.slots[static_cast<size_t>(pair) * d + col] = w * acc[i];
+      p.slots[static_cast<size_t>(pair) * d + n0 + r] = w * (acc[i] + half_acc[slice][lane][i]);
     }
   }
 }
 
 template <typename KernelT>
-void allow_big_lds(KernelT kernel, size_t bytes) {
-  if (bytes > 65536)
+void allow_lds(KernelT kernel, size_t bytes) {
+  if (bytes > 48 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
@@ -177,29 +218,29 @@ void allow_big_lds(KernelT kernel, size_t bytes) {
 }  // namespace
 
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  const dim3 grid((a.F + 16 * kWaves - 1) / (16 * kWaves), max_tiles);
+  const dim3 grid((a.F + 31) / 32, max_tiles);
   const size_t es = dtype == 1 ? 2 : 4;
   const size_t smem = kTileM * (a.d + 16 / es) * es;
   if (dtype == 1) {
-    allow_big_lds(k_gate_up<bf16_t>, smem);
-    hipLaunchKernelGGL(k_gate_up<bf16_t>, grid, dim3(64 * kWaves), smem, s, a);
+    allow_lds(k_gate_up<bf16_t>, smem);
+    hipLaunchKernelGGL(k_gate_up<bf16_t>, grid, dim3(kThreads), smem, s, a);
   } else {
-    allow_big_lds(k_gate_up<float>, smem);
-    hipLaunchKernelGGL(k_gate_up<float>, grid, dim3(64 * kWaves), smem, s, a);
+    allow_lds(k_gate_up<float>, smem);
+    hipLaunchKernelGGL(k_gate_up<float>, grid, dim3(kThreads), smem, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  const dim3 grid((a.d + 16 * kWaves - 1) / (16 * kWaves), max_tiles);
+  const dim3 grid((a.d + 31) / 32, max_tiles);
   const size_t es = dtype == 1 ? 2 : 4;
   const size_t smem = kTileM * (a.F + 16 / es) * es;
   if (dtype == 1) {
-    allow_big_lds(k_down<bf16_t>, smem);
-    hipLaunchKernelGGL(k_down<bf16_t>, grid, dim3(64 * kWaves), smem, s, a);
+    allow_lds(k_down<bf16_t>, smem);
+    hipLaunchKernelGGL(k_down<bf16_t>, grid, dim3(kThreads), smem, s, a);
   } else {
-    allow_big_lds(k_down<float>, smem);
-    hipLaunchKernelGGL(k_down<float>, grid, dim3(64 * kWaves), smem, s, a);
+    allow_lds(k_down<float>, smem);
+    hipLaunchKernelGGL(k_down<float>, grid, dim3(kThreads), smem, s, a);
   }
   return hipGetLastError();
 }

@@ -15,9 +15,9 @@ namespace mv {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kSlices = 4;   // 16-row vocabulary slices per wavefront
-constexpr int kUnroll = 8;
+constexpr int kLmWaves = 4;
+constexpr int kLmSlices = 4;   // 16-row vocabulary slices per wavefront
+constexpr int kLmUnroll = 8;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   const int m = min(kTileM, p.T - r0);
   const int d = p.d, nvec = d / VN, lda = d + VN;
   T *A = reinterpret_cast<T *>(smem);
-  __shared__ unsigned long long red[kWaves][kTileM];
+  __shared__ unsigned long long red[kLmWaves][kTileM];
 
   const T *xf = static_cast<const T *>(p.xf);
   for (int i = threadIdx.x; i < kTileM * nvec; i += blockDim.x) {
@@ -43,20 +43,20 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   const T *ar = A + (lane & 15) * lda + koff;
   const int nwin = d / WIN;
   uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
-  const int vbase = (blockIdx.x * kWaves + wv) * 16 * kSlices;
-  for (int sl = 0; sl < kSlices; ++sl) {
+  const int vbase = (blockIdx.x * kLmWaves + wv) * 16 * kLmSlices;
+  for (int sl = 0; sl < kLmSlices; ++sl) {
     const int v0 = vbase + sl * 16;
     if (v0 >= p.V) break;
     const int v = v0 + (lane & 15);
     const T *b = static_cast<const T *>(p.w) + static_cast<size_t>(min(v, p.V - 1)) * d + koff;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int w0 = 0; w0 < nwin; w0 += kUnroll) {
-      uint4 q[kUnroll];
+    for (int w0 = 0; w0 < nwin; w0 += kLmUnroll) {
+      uint4 q[kLmUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kLmUnroll; ++u)
         if (w0 + u < nwin) q[u] = ld16(b + (w0 + u) * WIN);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kLmUnroll; ++u)
         if (w0 + u < nwin) mfma16(acc, ld16(ar + (w0 + u) * WIN), q[u], T());
     }
     if (v < p.V) {
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   if (threadIdx.x < m) {
     uint64_t k = 0ull;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) k = red[w][threadIdx.x] > k ? red[w][threadIdx.x] : k;
+    for (int w = 0; w < kLmWaves; ++w) k = red[w][threadIdx.x] > k ? red[w][threadIdx.x] : k;
     if (k != 0ull) atomicMax(p.argkey + r0 + threadIdx.x, static_cast<unsigned long long>(k));
   }
 }
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void k_accept(AcceptArgs p) {
 }  // namespace
 
 hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s) {
-  const int rows_per_block = 16 * kSlices * kWaves;
+  const int rows_per_block = 16 * kLmSlices * kLmWaves;
   const dim3 grid((a.V + rows_per_block - 1) / rows_per_block, (a.T + kTileM - 1) / kTileM);
   const size_t es = dtype == 1 ? 2 : 4;
   const size_t smem = kTileM * (a.d + 16 / es) * es;
@@ -120,9 +120,9 @@ hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s) {
     (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   }
   if (dtype == 1)
-    hipLaunchKernelGGL(k_lm_argmax<bf16_t>, grid, dim3(64 * kWaves), smem, s, a);
+    hipLaunchKernelGGL(k_lm_argmax<bf16_t>, grid, dim3(64 * kLmWaves), smem, s, a);
   else
-    hipLaunchKernelGGL(k_lm_argmax<float>, grid, dim3(64 * kWaves), smem, s, a);
+    hipLaunchKernelGGL(k_lm_argmax<float>, grid, dim3(64 * kLmWaves), smem, s, a);
   return hipGetLastError();
 }
 

@@ -7,32 +7,43 @@
 
 namespace mv {
 
-// Rows of one expert tile of the grouped expert kernels.
+// Rows of one expert tile of the grouped expert kernels, and tokens of one
+// routing tile.
 constexpr int kTileM = 16;
+// Up to this many token rows a step takes the small-batch path: one routing
+// block per token, and every gate/up block groups the (token, slot) pairs by
+// expert itself instead of a separate grouping kernel.
+constexpr int kSmallT = 64;
+// Largest expert count (routed + shared) and slots per token supported.
+constexpr int kMaxExperts = 64 + 4;
+constexpr int kMaxSlots = 8 + 4;
 
-enum PrologueMode {
-  kRoute = 0,    // [combine] -> RMSNorm -> router -> top-k (+ permute if one block)
-  kFinal = 1,    // combine -> final RMSNorm -> x_f; clears the argmax keys
-  kCombine = 2,  // combine only: h_out = h + y
+enum RouteMode {
+  kRoute = 0,    // RMSNorm -> router -> top-k (-> permutation)
+  kFinal = 1,    // final RMSNorm -> x_f; clears the argmax keys
+  kCombine = 2,  // combine only
 };
 
-struct PrologueArgs {
-  int T, d, E, S, k, nslot, mode, tile_m;
+struct RouteArgs {
+  int T, d, E, S, k, nslot, mode;
   float eps;
-  const void *h_src;       // [T, d] residual input
-  void *h_dst;             // [T, d] (h_src + y) or copy of h_src; may be null
-  const float *slots;      // [T*nslot, d] previous layer's expert outputs; null: no combine
-  float *y_moe;            // [T, d] fp32 sum of slots (optional)
-  const void *gamma;       // [d]
-  void *x_out;             // [T, d]
-  const void *router_w;    // [E, d]
-  const float *router_b;   // [E] or null
-  int *ids;                // [T, k]
-  float *gates;            // [T, k]
-  unsigned long long *argkey;  // [T], cleared in kFinal mode
-  int *seg;                // [E+S+1] row offset of each expert segment
-  int *tile_start;         // [E+S+1] first tile of each expert
-  int *rows;               // [T*nslot] pair id of each sorted row
+  const void *gamma;        // [d]
+  void *x_out;              // [T, d]
+  const void *router_w;     // [E, d]
+  const float *router_b;    // [E] or null
+  int *ids;                 // [T, k]
+  float *gates;             // [T, k]
+  int *seg, *tile_start, *rows;
+  int4 *tile_info;          // [max tiles] (expert, first row, rows, 0) per 16-row tile
+  unsigned long long *argkey;  // kFinal: cleared
+};
+
+// Combine of the previous layer's expert slots into the hidden state.
+struct CombineArgs {
+  const void *h_src;        // [T, d] residual input
+  void *h_dst;              // [T, d] h_src + y (may alias h_src)
+  const float *slots;       // [T*nslot, d]; null: no combine (h_dst unused)
+  float *y_moe;             // [T, d] optional
 };
 
 struct ExpertArgs {
@@ -42,7 +53,10 @@ struct ExpertArgs {
   void *a_out;
   const void *w_routed;    // this layer's routed block: [E, 2F, d] or [E, d, F]
   const void *w_shared;    // this layer's shared block: [S, 2F, d] or [S, d, F]
-  const int *seg, *tile_start, *rows;
+  const int *ids;          // [T, k] routing (grouped in-block on the small path)
+  int group_in_block;      // small path: gate/up groups the pairs (block (0,0) writes them)
+  int *seg, *tile_start, *rows;
+  int4 *tile_info;         // [max tiles] (expert, first row, rows, 0)
   const float *gates;      // [T, k]
   float *slots;            // [T*nslot, d]
 };
@@ -64,14 +78,11 @@ struct AcceptArgs {
 };
 
 // dtype-dispatched launchers (dtype: 0 fp32, 1 bf16); return the launch error.
-hipError_t launch_prologue(int dtype, const PrologueArgs &a, hipStream_t s);
-hipError_t launch_permute(const PrologueArgs &a, hipStream_t s);
+hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int ntok, hipStream_t s);
+hipError_t launch_permute(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t s);
-
-// Tokens handled by one prologue block (one wavefront per token).
-constexpr int kPrologueTokens = 4;
 
 }  // namespace mv

@@ -1,0 +1,297 @@
+// Per-token routing core.  Every routing kernel runs this code, with one or
+// sixteen tokens per block, so a token's results do not depend on the batch
+// it is in.  Canonical arithmetic (chunk = one 16-byte vector: 8 bf16 or 4
+// fp32 elements of a row):
+//   combine   h' = round(h + y),  y = sum of the token's slots in slot order
+//             (routed slots in selection order, then the shared ones)
+//   sumsq     chunk partial p_c = sequential sum of h'^2 over chunk c; lane l
+//             of one wavefront sums p_c for c = l, l+64, ... in order; then a
+//             xor butterfly (32, 16, 8, 4, 2, 1); lane 0's value
+//   RMSNorm   x = round((h' * (sumsq/d + eps)^-1/2) * gamma)
+//   router    16 lanes per expert: lane q sums, in one fp32 FMA chain, the
+//             chunks c = q, q+16, ... of x * W_r[e]; xor butterfly (1, 2, 4,
+//             8); lane q = 0's value, + optional bias
+//   top-k     experts ordered by (logit desc, id asc); gates = softmax over
+//             the k selected logits, denominator summed in rank order
+// Routing follows the architecture paragraph of "Jina AI Releases jina-ocr-v1,
+// a 3.4B MoE Document Parser With Built-In Speculative Decoding"
+// (ainewsfeed.tech): 64 routed experts, top-6, two shared experts.
+#pragma once
+
+#include "mv_common.h"
+#include "mv_internal.h"
+
+namespace mv {
+
+constexpr int kRouteThreads = 1024;  // 16 wavefronts: wavefront w owns experts 4w..4w+3
+constexpr int kRouterChunks = 10;    // router chunks per lane held in registers (d <= 1280 bf16)
+
+// Router weights of one wavefront's four experts (e = e_base + (lane >> 4)):
+// lane q = lane & 15 holds the chunks c = q, q+16, ... of its expert's row.
+template <typename T>
+__device__ __forceinline__ void router_preload(uint4 *wq, const T *w_router, int E, int e_base, int d) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63, q = lane & 15;
+  const int e = min(e_base + (lane >> 4), E - 1);
+  const T *wr = w_router + static_cast<size_t>(e) * d;
+  const int nvec = d / VN;
+#pragma unroll
+  for (int i = 0; i < kRouterChunks; ++i)
+    if (q + 16 * i < nvec) wq[i] = ld16(wr + (q + 16 * i) * VN);
+}
+
+// Router logits of tokens [0, nt) of the x rows in LDS (x_lds[t*ldx + j]).
+template <typename T>
+__device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int ldx, int nt, int d,
+                                            const T *w_router, const float *bias, int E, int e_base,
+                                            float *lg) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63, q = lane & 15;
+  const int e = e_base + (lane >> 4);
+  const int nvec = d / VN;
+  const T *wr = w_router + static_cast<size_t>(min(e, E - 1)) * d;
+  const float b = (bias && e < E) ? bias[e] : 0.f;
+  for (int t = 0; t < nt; ++t) {
+    const T *xr = x_lds + t * ldx;
+    float acc = 0.f;
+    auto accumulate = [&](const uint4 &wv, int c) {
+      float w[VN], x[VN];
+      unpack(wv, w, T());
+      unpack(ld16(xr + c * VN), x, T());
+#pragma unroll
+      for (int j = 0; j < VN; ++j) acc += x[j] * w[j];
+    };
+#pragma unroll
+    for (int i = 0; i < kRouterChunks; ++i)
+      if (q + 16 * i < nvec) accumulate(wq[i], q + 16 * i);
+    for (int c = q + 16 * kRouterChunks; c < nvec; c += 16) accumulate(ld16(wr + c * VN), c);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+    if (q == 0 && e < 64) lg[t * 64 + e] = acc + b;
+  }
+}
+
+// Top-k of one token's logits lg_row[0..E) on one wavefront: lane e's rank
+// is the number of experts ordered before it by (logit desc, id asc).
+__device__ __forceinline__ void select_top_k(const float *lg_row, float *sel_lds, int E, int k,
+                                             int *ids, float *gates) {
+  const int lane = threadIdx.x & 63;
+  const float logit = lg_row[lane];
+  const uint64_t mine = argmax_key(logit, static_cast<uint32_t>(lane));
+  int rank = 0;
+#pragma unroll 16
+  for (int j = 0; j < E; ++j) rank += argmax_key(lg_row[j], static_cast<uint32_t>(j)) > mine;
+  const bool chosen = lane < E && rank < k;
+  const uint64_t top = __ballot(chosen && rank == 0);
+  const float vmax = __shfl(logit, static_cast<int>(__builtin_ctzll(top)));
+  const float ex = expf(logit - vmax);
+  if (chosen) {
+    sel_lds[rank] = ex;
+    ids[rank] = lane;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float den = 0.f;
+  for (int s = 0; s < k; ++s) den += sel_lds[s];
+  if (chosen) gates[rank] = ex / den;
+}
+
+// LDS layout of a routing block holding `ntok` token rows.
+struct RouteSmem {
+  size_t h, p, lg, inv, sel, total;
+};
+__host__ __device__ inline RouteSmem route_smem(int ntok, int d, int elem_bytes) {
+  const int vn = 16 / elem_bytes, nvec = d / vn;
+  RouteSmem s;
+  s.h = 0;                                                        // [ntok][d + vn] storage T
+  s.p = s.h + static_cast<size_t>(ntok) * (d + vn) * elem_bytes;  // [ntok][nvec] fp32 partials
+  s.lg = s.p + static_cast<size_t>(ntok) * nvec * 4;              // [ntok][64] logits
+  s.inv = s.lg + static_cast<size_t>(ntok) * 64 * 4;              // [ntok]
+  s.sel = s.inv + static_cast<size_t>(ntok) * 4;                  // [ntok][8]
+  s.total = s.sel + static_cast<size_t>(ntok) * 8 * 4;
+  return s;
+}
+
+// Routes tokens [t0, t0 + nt) (nt <= ntok) with one block of kRouteThreads.
+template <typename T>
+__device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, int nt, int ntok,
+                            unsigned char *smem) {
+  constexpr int VN = Vec<T>::N;
+  const int d = a.d, nvec = d / VN, ld = d + VN;
+  const RouteSmem L = route_smem(ntok, d, sizeof(T));
+  T *hl = reinterpret_cast<T *>(smem + L.h);
+  float *pl = reinterpret_cast<float *>(smem + L.p);
+  float *lg = reinterpret_cast<float *>(smem + L.lg);
+  float *inv = reinterpret_cast<float *>(smem + L.inv);
+  float *sel = reinterpret_cast<float *>(smem + L.sel);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  // router weights first: their latency overlaps the combine and the norm
+  uint4 wq[kRouterChunks];
+  if (a.mode == kRoute) router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, 4 * wv, d);
+
+  // combine (or plain load) of the rows, chunk partial sums of squares
+  const T *hs = static_cast<const T *>(c.h_src);
+  for (int it = tid; it < nt * nvec; it += blockDim.x) {
+    const int r = it / nvec, ch = it % nvec, t = t0 + r;
+    float h[VN];
+    unpack(ld16(hs + static_cast<size_t>(t) * d + ch * VN), h, T());
+    if (c.slots) {
+      float y[VN];
+#pragma unroll
+      for (int i = 0; i < VN; ++i) y[i] = 0.f;
+      const float *sp = c.slots + static_cast<size_t>(t) * a.nslot * d + ch * VN;
+      for (int s = 0; s < a.nslot; ++s) {
+#pragma unroll
+        for (int i = 0; i < VN; i += 4) {
+          const float4 v = *reinterpret_cast<const float4 *>(sp + static_cast<size_t>(s) * d + i);
+          y[i] += v.x; y[i + 1] += v.y; y[i + 2] += v.z; y[i + 3] += v.w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < VN; ++i) h[i] = round_to<T>(h[i] + y[i]);
+      if (c.y_moe) {
+        float *yp = c.y_moe + static_cast<size_t>(t) * d + ch * VN;
+#pragma unroll
+        for (int i = 0; i < VN; i += 4)
+          *reinterpret_cast<float4 *>(yp + i) = make_float4(y[i], y[i + 1], y[i + 2], y[i + 3]);
+      }
+    }
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < VN; ++i) p += h[i] * h[i];
+    const uint4 pk = pack(h, T());
+    st16(hl + r * ld + ch * VN, pk);
+    if (c.slots && c.h_dst) st16(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + ch * VN, pk);
+    pl[r * nvec + ch] = p;
+  }
+  if (a.mode == kCombine) return;
+  __syncthreads();
+
+  // per-token sum of squares (wavefront r handles token r) and 1/rms
+  for (int r = wv; r < nt; r += blockDim.x / kWave) {
+    float acc = 0.f;
+    for (int ch = lane; ch < nvec; ch += kWave) acc += pl[r * nvec + ch];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) inv[r] = 1.0f / sqrtf(acc / static_cast<float>(d) + a.eps);
+  }
+  __syncthreads();
+
+  // x = round(h * inv * gamma): to LDS (router operand) and to x_out
+  const T *gam = static_cast<const T *>(a.gamma);
+  T *xo = static_cast<T *>(a.x_out);
+  for (int it = tid; it < nt * nvec; it += blockDim.x) {
+    const int r = it / nvec, ch = it % nvec;
+    float hv[VN], g[VN], x[VN];
+    unpack(ld16(hl + r * ld + ch * VN), hv, T());
+    unpack(ld16(gam + ch * VN), g, T());
+    const float s = inv[r];
+#pragma unroll
+    for (int i = 0; i < VN; ++i) x[i] = round_to<T>((hv[i] * s) * g[i]);
+    const uint4 pk = pack(x, T());
+    st16(hl + r * ld + ch * VN, pk);
+    st16(xo + static_cast<size_t>(t0 + r) * d + ch * VN, pk);
+  }
+  if (a.mode == kFinal) {
+    if (tid < nt) a.argkey[t0 + tid] = 0ull;
+    return;
+  }
+  __syncthreads();
+
+  if (4 * wv < a.E)
+    router_rows<T>(wq, hl, ld, nt, d, static_cast<const T *>(a.router_w), a.router_b, a.E, 4 * wv, lg);
+  __syncthreads();
+  for (int r = wv; r < nt; r += blockDim.x / kWave)
+    select_top_k(lg + r * 64, sel + r * 8, a.E, a.k, a.ids + (t0 + r) * a.k, a.gates + (t0 + r) * a.k);
+}
+
+// ---------------------------------------------------------------- grouping
+
+// Where the grouping of (token, slot) pairs by expert is written.
+struct GroupOut {
+  int *seg;         // [E+S+1] first row of each expert segment
+  int *tile_start;  // [E+S+1] first tile of each expert
+  int *rows;        // [T*nslot] pair id (t*nslot + slot) of each sorted row
+  int4 *tile_info;  // [tiles] (expert, first row, rows, 0), or null
+};
+
+// Stable grouping of the T*k routed pairs by expert on one wavefront: for
+// each expert present, a ballot over 64 pairs at a time gives both the count
+// and each pair's rank among the earlier pairs of its expert.  Shared expert s gets
+// segment E + s holding every token.  Requires E <= 64.  `ids` and every
+// output may be in global memory or in LDS.
+__device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, int nslot, int tile_m,
+                                   const GroupOut &o) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const int np = T * k;
+  // Experts are visited in order of their first pair in each group of 64
+  // pairs (only experts that occur); counts and ranks do not depend on the
+  // visiting order.
+  int cnt = 0;  // lane e: pairs routed to expert e
+  for (int base = 0; base < np; base += kWave) {
+    const int q = base + lane;
+    const int e_q = q < np ? ids[q] : -1;
+    uint64_t left = __ballot(q < np);
+    while (left) {
+      const int e = __builtin_amdgcn_readlane(e_q, static_cast<int>(__builtin_ctzll(left)));
+      const uint64_t m = __ballot(e_q == e);
+      left &= ~m;
+      if (lane == e) cnt += __popcll(m);
+    }
+  }
+  // exclusive scans over the experts (lanes) of counts and tile counts
+  const int tiles = lane < E ? (cnt + tile_m - 1) / tile_m : 0;
+  int sc = lane < E ? cnt : 0, st = tiles;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int vc = __shfl_up(sc, off), vt = __shfl_up(st, off);
+    if (lane >= off) { sc += vc; st += vt; }
+  }
+  const int seg_e = sc - (lane < E ? cnt : 0), tile_e = st - tiles;
+  const int routed_total = __builtin_amdgcn_readlane(sc, kWave - 1);
+  const int routed_tiles = __builtin_amdgcn_readlane(st, kWave - 1);
+  if (lane < E) {
+    o.seg[lane] = seg_e;
+    o.tile_start[lane] = tile_e;
+  }
+  const int shared_tiles = (T + tile_m - 1) / tile_m;
+  if (lane <= S) {
+    o.seg[E + lane] = routed_total + lane * T;
+    o.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
+  }
+  // scatter routed pairs, ascending pair order inside each expert
+  int next = seg_e;  // lane e: next free row of expert e's segment
+  for (int base = 0; base < np; base += kWave) {
+    const int q = base + lane;
+    const int e_q = q < np ? ids[q] : -1;
+    int pos = -1;
+    uint64_t left = __ballot(q < np);
+    while (left) {
+      const int e = __builtin_amdgcn_readlane(e_q, static_cast<int>(__builtin_ctzll(left)));
+      const uint64_t m = __ballot(e_q == e);
+      left &= ~m;
+      const int start = __builtin_amdgcn_readlane(next, e);
+      if (e_q == e) pos = start + __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == e) next += __popcll(m);
+    }
+    if (q < np) o.rows[pos] = (q / k) * nslot + (q % k);
+  }
+  for (int j = lane; j < S * T; j += kWave) {
+    const int s = j / T, t = j % T;
+    o.rows[routed_total + s * T + t] = t * nslot + k + s;
+  }
+  if (o.tile_info) {
+    if (lane < E)
+      for (int j = 0; j < tiles; ++j)
+        o.tile_info[tile_e + j] = make_int4(lane, seg_e + j * tile_m, min(tile_m, cnt - j * tile_m), 0);
+    for (int s = 0; s < S; ++s)
+      for (int j = lane; j < shared_tiles; j += kWave)
+        o.tile_info[routed_tiles + s * shared_tiles + j] =
+            make_int4(E + s, routed_total + s * T + j * tile_m, min(tile_m, T - j * tile_m), 0);
+  }
+}
+
+}  // namespace mv

@@ -113,7 +113,7 @@ def _layer_check(bd, torch, dims, W, model, layer, h, label):
     return out
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 37, 130])
+@pytest.mark.parametrize("T", [1, 5, 16, 37, 64, 65, 130])
 def test_layer_forward_tiny_fp32(bd, torch_cuda, tiny, T):
     dims, W, model = tiny
     h = synth.make_hidden(dims, T, seed=100 + T)
@@ -270,6 +270,25 @@ def test_deterministic_and_batch_invariant(bd, torch_cuda, big):
     assert np.array_equal(_host(bd, a["h_out"])[rows], _host(bd, c["h_out"]))
     assert np.array_equal(_host(bd, a["argmax"])[rows], _host(bd, c["argmax"]))
     assert np.array_equal(_host(bd, a["topk_ids"])[:, rows], _host(bd, c["topk_ids"]))
+
+
+@pytest.mark.parametrize("model_name", ["tiny", "big"])
+def test_same_results_on_both_batch_paths(bd, torch_cuda, tiny, big, model_name):
+    """Up to 64 rows use the single-block routing path with the combine fused
+    into the down kernel; more rows use tiled routing kernels.  Both do the
+    same arithmetic in the same order, so a sequence's results are
+    bit-identical whichever path its batch takes."""
+    dims, W, model = tiny if model_name == "tiny" else big
+    K = 3
+    h = synth.make_hidden(dims, 17 * (K + 1), seed=91)
+    drafts = np.random.default_rng(2).integers(0, dims.vocab, (17, K)).astype(np.int32)
+    small = bd.run_verify_step(model, _dev(bd, h[:64]), _dev(bd, drafts[:16]), 16, K, routing=True)
+    large = bd.run_verify_step(model, _dev(bd, h), _dev(bd, drafts), 17, K, routing=True)
+    _sync(torch_cuda)
+    for key in ("h_out", "argmax", "committed", "n_committed"):
+        assert np.array_equal(_host(bd, small[key]), _host(bd, large[key])[:16 if key in (
+            "committed", "n_committed") else 64]), key
+    assert np.array_equal(_host(bd, small["topk_ids"]), _host(bd, large["topk_ids"])[:, :64])
 
 
 def test_lossless_gpu_decode_loop(bd, torch_cuda, tiny):
