@@ -33,7 +33,7 @@ int max_tiles(const mv_config &c, int T) {
 }
 
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, total;
+  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, arrive, total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -58,6 +58,7 @@ Layout layout(const mv_config &c, int T) {
   L.a = take(static_cast<size_t>(T) * nslot * c.d_ff * es);
   L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
   L.argkey = take(static_cast<size_t>(T) * 8);
+  L.arrive = take(static_cast<size_t>(c.n_layers) * 4);
   L.total = off;
   return L;
 }
@@ -138,6 +139,10 @@ struct Step {
   float *slots() const { return reinterpret_cast<float *>(ws + L.slots); }
   float *gates() const { return reinterpret_cast<float *>(ws + L.gates); }
   unsigned long long *argkey() const { return reinterpret_cast<unsigned long long *>(ws + L.argkey); }
+  unsigned *arrive() const { return reinterpret_cast<unsigned *>(ws + L.arrive); }
+  // Layers >= 1 of a step with at most kGroupInRouteT rows are grouped by the
+  // routing kernel (arrival counter per layer, cleared by layer 0's gate/up).
+  bool group_in_route(int layer, bool step) const { return step && layer > 0 && T <= mv::kGroupInRouteT; }
 
   mv::RouteArgs route_args(int layer, int mode, int *ids, float *gates_out) const {
     mv::RouteArgs a{};
@@ -173,8 +178,9 @@ struct Step {
   // One routing launch (+ the grouping kernel on the large-batch path).
   // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
   int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
-            float *y_moe, int *ids, float *gates_out) const {
-    const mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
+            float *y_moe, int *ids, float *gates_out, bool step = false) const {
+    mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
+    if (mode == mv::kRoute && group_in_route(layer, step)) a.arrive = arrive() + layer;
     mv::CombineArgs cb{};
     cb.h_src = h_src;
     cb.h_dst = h_dst;
@@ -186,7 +192,7 @@ struct Step {
   }
 
   // gate/up then down for `layer`, leaving the weighted expert outputs in slots.
-  int ffn(int layer, const int *ids_in, const float *gates_in) const {
+  int ffn(int layer, const int *ids_in, const float *gates_in, bool step = false) const {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e{};
     e.T = T;
@@ -204,7 +210,11 @@ struct Step {
     e.rows = rows();
     e.tile_info = tinfo();
     e.ids = ids_in;
-    e.group_in_block = small() ? 1 : 0;
+    e.group_in_block = small() && !group_in_route(layer, step) ? 1 : 0;
+    if (step && layer == 0 && T <= mv::kGroupInRouteT) {
+      e.zero_cnt = arrive();
+      e.n_zero = c.n_layers;
+    }
     e.gates = gates_in;
     e.slots = slots();
     const int mt = max_tiles(c, T);
@@ -279,10 +289,11 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
                             : reinterpret_cast<int *>(st.ws + st.L.ids);
     // layer 0 routes h_in; later layers first add the previous layer's experts
     if (layer == 0)
-      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates);
+      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, true);
     else
-      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates);
-    if (rc || (rc = st.ffn(layer, ids, gates))) return rc;
+      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates,
+                    true);
+    if (rc || (rc = st.ffn(layer, ids, gates, true))) return rc;
   }
   if ((rc = st.route(L - 1, mv::kFinal, L == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, nullptr,
                      nullptr)))

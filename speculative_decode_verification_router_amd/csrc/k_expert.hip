@@ -66,6 +66,7 @@ __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b,
 
 // Grouping of a small batch, built in LDS by every gate/up block.
 struct Grouping {
+  int cnt[kWave], run[kWave];
   int seg[kMaxExperts + 1];
   int tile_start[kMaxExperts + 1];
   int rows[kSmallT * kMaxSlots];
@@ -84,9 +85,10 @@ __device__ bool block_tile(const ExpertArgs &p, int tile, TileInfo &ti, Grouping
     return true;
   }
   const GroupOut lds{g.seg, g.tile_start, g.rows, nullptr};
-  group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds);
+  group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds, g.cnt, g.run);
   __syncthreads();
   if (write_global) {  // the grouping of record, for the down kernel
+    for (int i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero_cnt[i] = 0u;
     for (int i = threadIdx.x; i <= ne; i += blockDim.x) {
       p.seg[i] = g.seg[i];
       p.tile_start[i] = g.tile_start[i];

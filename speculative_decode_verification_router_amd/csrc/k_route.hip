@@ -18,13 +18,29 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, CombineArgs c, int ntok) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int last;
+  __shared__ int cnt_lds[kWave], run_lds[kWave];
   const int t0 = blockIdx.x * ntok;
   route_block<T>(a, c, t0, min(ntok, a.T - t0), ntok, smem);
+  if (!a.arrive || a.mode != kRoute) return;
+  // publish this block's routing; the last block to arrive groups the pairs
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    last = __hip_atomic_fetch_add(a.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last || threadIdx.x >= kWave) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const GroupOut o{a.seg, a.tile_start, a.rows, a.tile_info};
+  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, kTileM, o, cnt_lds, run_lds);
 }
 
 __global__ __launch_bounds__(64) void k_group(RouteArgs a) {
+  __shared__ int cnt_lds[kWave], run_lds[kWave];
   const GroupOut o{a.seg, a.tile_start, a.rows, a.tile_info};
-  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, kTileM, o);
+  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, kTileM, o, cnt_lds, run_lds);
 }
 
 __global__ __launch_bounds__(256) void k_permute_large(RouteArgs p) {

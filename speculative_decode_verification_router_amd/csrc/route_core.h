@@ -217,40 +217,51 @@ struct GroupOut {
   int4 *tile_info;  // [tiles] (expert, first row, rows, 0), or null
 };
 
-// Stable grouping of the T*k routed pairs by expert on one wavefront: for
-// each expert present, a ballot over 64 pairs at a time gives both the count
-// and each pair's rank among the earlier pairs of its expert.  Shared expert s gets
-// segment E + s holding every token.  Requires E <= 64.  `ids` and every
-// output may be in global memory or in LDS.
+// Lanes of this wavefront whose value equals this lane's (values < 128),
+// from seven ballots over the bits of the value.
+__device__ __forceinline__ uint64_t match_lanes(int v, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const bool bit = (v >> b) & 1;
+    const uint64_t on = __ballot(valid && bit);
+    m &= bit ? on : ~on;
+  }
+  return valid ? m : 0ull;
+}
+
+// Stable grouping of the T*k routed pairs by expert on one wavefront, 64
+// pairs at a time: a pair's same-expert lanes give its rank among the
+// earlier pairs of its expert and, for the first of them, the count.
+// Shared expert s gets segment E + s holding every token.  Requires E <= 64
+// and `cnt_lds`, `run_lds` (LDS, >= 64 ints each).  `ids` and every output
+// may be in global memory or in LDS.
 __device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, int nslot, int tile_m,
-                                   const GroupOut &o) {
+                                   const GroupOut &o, int *cnt_lds, int *run_lds) {
   if (threadIdx.x >= kWave) return;
   const int lane = threadIdx.x;
   const int np = T * k;
-  // Experts are visited in order of their first pair in each group of 64
-  // pairs (only experts that occur); counts and ranks do not depend on the
-  // visiting order.
-  int cnt = 0;  // lane e: pairs routed to expert e
+  const uint64_t below = (1ull << lane) - 1ull;
+  cnt_lds[lane] = 0;
+  run_lds[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
   for (int base = 0; base < np; base += kWave) {
     const int q = base + lane;
-    const int e_q = q < np ? ids[q] : -1;
-    uint64_t left = __ballot(q < np);
-    while (left) {
-      const int e = __builtin_amdgcn_readlane(e_q, static_cast<int>(__builtin_ctzll(left)));
-      const uint64_t m = __ballot(e_q == e);
-      left &= ~m;
-      if (lane == e) cnt += __popcll(m);
-    }
+    const int e_q = q < np ? ids[q] : 0;
+    const uint64_t m = match_lanes(e_q, q < np);
+    if (q < np && (m & below) == 0) cnt_lds[e_q] += __popcll(m);  // first lane of its expert
+    __builtin_amdgcn_wave_barrier();
   }
   // exclusive scans over the experts (lanes) of counts and tile counts
-  const int tiles = lane < E ? (cnt + tile_m - 1) / tile_m : 0;
-  int sc = lane < E ? cnt : 0, st = tiles;
+  const int cnt = lane < E ? cnt_lds[lane] : 0;
+  const int tiles = (cnt + tile_m - 1) / tile_m;
+  int sc = cnt, st = tiles;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const int vc = __shfl_up(sc, off), vt = __shfl_up(st, off);
     if (lane >= off) { sc += vc; st += vt; }
   }
-  const int seg_e = sc - (lane < E ? cnt : 0), tile_e = st - tiles;
+  const int seg_e = sc - cnt, tile_e = st - tiles;
   const int routed_total = __builtin_amdgcn_readlane(sc, kWave - 1);
   const int routed_tiles = __builtin_amdgcn_readlane(st, kWave - 1);
   if (lane < E) {
@@ -262,22 +273,17 @@ __device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, i
     o.seg[E + lane] = routed_total + lane * T;
     o.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
   }
+  run_lds[lane] = seg_e;  // next free row of expert `lane`
+  __builtin_amdgcn_wave_barrier();
   // scatter routed pairs, ascending pair order inside each expert
-  int next = seg_e;  // lane e: next free row of expert e's segment
   for (int base = 0; base < np; base += kWave) {
     const int q = base + lane;
-    const int e_q = q < np ? ids[q] : -1;
-    int pos = -1;
-    uint64_t left = __ballot(q < np);
-    while (left) {
-      const int e = __builtin_amdgcn_readlane(e_q, static_cast<int>(__builtin_ctzll(left)));
-      const uint64_t m = __ballot(e_q == e);
-      left &= ~m;
-      const int start = __builtin_amdgcn_readlane(next, e);
-      if (e_q == e) pos = start + __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == e) next += __popcll(m);
-    }
-    if (q < np) o.rows[pos] = (q / k) * nslot + (q % k);
+    const int e_q = q < np ? ids[q] : 0;
+    const uint64_t m = match_lanes(e_q, q < np);
+    if (q < np) o.rows[run_lds[e_q] + __popcll(m & below)] = (q / k) * nslot + (q % k);
+    __builtin_amdgcn_wave_barrier();
+    if (q < np && (m & below) == 0) run_lds[e_q] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
   }
   for (int j = lane; j < S * T; j += kWave) {
     const int s = j / T, t = j % T;
