@@ -68,6 +68,13 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time graph replays")
+    ap.add_argument("--cpu-baseline-rows", type=int, default=8,
+                    help="stack workloads: rows the oracle pushes through the stack")
+    ap.add_argument("--loop", action="store_true",
+                    help="run the decode loop (sequences until --loop-tokens committed each)")
+    ap.add_argument("--loop-tokens", type=int, default=1085)
+    ap.add_argument("--k-draft", type=int, default=None)
+    ap.add_argument("--match-p", type=float, default=None)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device copies of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -95,14 +102,55 @@ def main(argv=None):
 
     bd.load()
     wl = synth.WORKLOADS[args.workload]
-    if wl.batch == 0:
-        raise SystemExit(f"{wl.name} has no LM head / drafts; not a verify-step workload")
-    dims = wl.dims
-    B, K = wl.batch, wl.k_draft
-    T = B * (K + 1)
     torch.cuda.set_device(0)
     print(f"[bench] generating {wl.name} weights", file=sys.stderr, flush=True)
     W = synth.workload_weights(wl, seed=args.seed)
+    if wl.batch == 0:
+        line = bench_stack(args, wl, W, bd, synth, torch)
+    elif args.loop:
+        line = bench_loop(args, wl, W, bd, synth, torch)
+    else:
+        line = bench_verify(args, wl, W, bd, synth, torch)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _timed(run, stream, steps, warmup, torch):
+    """Warm up, then time `steps` calls of run(stream) with events on `stream`."""
+    for _ in range(warmup):
+        run(stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        run(stream)
+    t_enq = time.perf_counter() - t0
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall, t_enq
+
+
+def _header(args, wl):
+    return {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
+
+
+def bench_verify(args, wl, W, bd, synth, torch):
+    dims = wl.dims
+    B, K = wl.batch, wl.k_draft
+    T = B * (K + 1)
     model = bd.DeviceModel(dims, W, max_tokens=T)
     h_np = synth.workload_hidden(wl, seed=args.seed)
     h = bd.to_device(h_np)
@@ -136,20 +184,7 @@ def main(argv=None):
             step(torch.cuda.current_stream())
         run = lambda stream: graph.replay()  # noqa: E731
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        run(stream)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        run(stream)
-    t_enq = time.perf_counter() - t0
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, wall, t_enq = _timed(run, stream, args.steps, args.warmup, torch)
     committed_per_step = int(bd.to_host(out["n_committed"]).sum())
     value = committed_per_step / (ms * 1e-3)
 
@@ -164,15 +199,13 @@ def main(argv=None):
         "algorithmic_bytes_per_step": int(nbytes),
         "distinct_experts_per_layer": distinct,
     }
-
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, W, h_np, drafts_np, args.cpu_baseline_steps)
-
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "committed tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "committed tokens/s"}
+    line.update(_header(args, wl))
+    line.update({
+        "ms_per_step": round(ms, 4),
         "data": "synthetic (seeded; weights N(0,0.02), hidden N(0,1), drafts = argmax w.p. p)",
         "config": {"workload": wl.name, "batch": B, "k_draft": K, "tokens": T,
                    "layers": dims.n_layers, "d_model": dims.d_model, "d_ff": dims.d_ff,
@@ -184,21 +217,171 @@ def main(argv=None):
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_ms_per_step": round(t_enq / args.steps * 1e3, 4),
         "graph": bool(args.graph),
-    }
-    print(json.dumps(line), flush=True)
-    return 0
+    })
+    return line
+
+
+def stack_flops(dims, T):
+    """Algorithmic flops of the MoE stack on T rows: router GEMV plus
+    gate/up and down of the k routed and S shared experts per row."""
+    d, F = dims.d_model, dims.d_ff
+    per_row = 2 * d * dims.n_routed + (dims.top_k + dims.n_shared) * (2 * d * 2 * F + 2 * F * d)
+    return dims.n_layers * T * per_row
+
+
+def bench_stack(args, wl, W, bd, synth, torch):
+    """Token batch through the 12-layer stack (no LM head): one step = one
+    pass of every layer, each a moe_layer_forward call; MFMA-bound."""
+    dims = wl.dims
+    T = wl.tokens
+    model = bd.DeviceModel(dims, W, max_tokens=T)
+    h_np = synth.workload_hidden(wl, seed=args.seed)
+    h0 = bd.to_device(h_np)
+    h1 = torch.empty_like(h0)
+
+    def step(stream):
+        for layer in range(dims.n_layers):
+            bd.moe_layer_forward(model.cfg, model.weights, layer, T, h0 if layer == 0 else h1, h1,
+                                 None, None, None, model.ws, model.ws_bytes, stream)
+
+    stream = torch.cuda.current_stream()
+    ms, wall, t_enq = _timed(step, stream, args.steps, args.warmup, torch)
+    flops = stack_flops(dims, T)
+    achieved = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+
+        rows = max(1, args.cpu_baseline_rows)
+        t0 = time.perf_counter()
+        O.forward_tokens(h_np[:rows], W, dims, lm_head=False)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(rows / dt, 3), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+               "sample": f"first {rows} of the {T} rows through all {dims.n_layers} layers "
+                         "(float64 numpy oracle; rows are independent)",
+               "s_per_row": round(dt / rows, 4)}
+    line = {"metric": "tokens/s through the 12-layer MoE stack + % of bf16 MFMA peak",
+            "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s"}
+    line.update(_header(args, wl))
+    line.update({
+        "ms_per_step": round(ms, 4),
+        "data": "synthetic (seeded; weights N(0,0.02), hidden N(0,1))",
+        "config": {"workload": wl.name, "tokens": T, "layers": dims.n_layers,
+                   "d_model": dims.d_model, "d_ff": dims.d_ff,
+                   "experts": f"{dims.n_routed} routed top-{dims.top_k} + {dims.n_shared} shared"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "whole stack (12 x moe_layer_forward)",
+                     "algorithmic_flops_per_step": flops},
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 4),
+        "host_enqueue_ms_per_step": round(t_enq / args.steps * 1e3, 4),
+    })
+    return line
+
+
+def bench_loop(args, wl, W, bd, synth, torch):
+    """Decode loop: every sequence runs until it has committed `loop_tokens`
+    tokens; each step's output hidden rows are the next step's input rows,
+    finished sequences drop out.  Drafts are drawn in an untimed rehearsal
+    of the same loop (the argmax does not depend on the drafts); the timed
+    replay includes the per-step host read of the commit counts."""
+    dims = wl.dims
+    K = args.k_draft if args.k_draft is not None else wl.k_draft
+    p = args.match_p if args.match_p is not None else wl.match_p
+    B0, target = wl.batch, args.loop_tokens
+    model = bd.DeviceModel(dims, W, max_tokens=B0 * (K + 1))
+    h_np = synth.make_hidden(dims, B0 * (K + 1), args.seed, wl.code)
+    h_start = bd.to_device(h_np)
+    bufs = [torch.empty_like(h_start), torch.empty_like(h_start)]
+    T_max = B0 * (K + 1)
+    outs = dict(argmax=torch.empty(T_max, dtype=torch.int32, device="cuda"),
+                n_accepted=torch.empty(B0, dtype=torch.int32, device="cuda"),
+                committed=torch.empty((B0, K + 1), dtype=torch.int32, device="cuda"),
+                n_committed=torch.empty(B0, dtype=torch.int32, device="cuda"))
+    zero = torch.zeros((B0, max(K, 1)), dtype=torch.int32, device="cuda")
+
+    def verify(h_in, h_out, drafts, B):
+        bd.moe_verify_step(model.cfg, model.weights, B, K, h_in, drafts, h_out, outs["argmax"],
+                           outs["n_accepted"], outs["committed"], outs["n_committed"], None,
+                           model.ws, model.ws_bytes, None)
+
+    def loop(plan=None):
+        """plan None: rehearse and record drafts; else replay them."""
+        done = np.zeros(B0, np.int64)
+        alive = np.arange(B0)
+        h_in = h_start
+        recorded, steps, rows, seq_steps, raw = [], 0, 0, 0, 0
+        while alive.size:
+            B = alive.size
+            T = B * (K + 1)
+            h_out = bufs[steps % 2][:T]
+            if plan is None:
+                verify(h_in[:T], h_out, zero, B)
+                g = bd.to_host(outs["argmax"][:T]).reshape(B, K + 1)
+                dr = synth.make_drafts(g, p, dims.vocab, seed=args.seed, step=steps, code=wl.code)
+                drafts = bd.to_device(dr)
+                recorded.append(drafts)
+            else:
+                drafts = plan[steps]
+            verify(h_in[:T], h_out, drafts, B)
+            n_com = bd.to_host(outs["n_committed"][:B])   # the host decides who goes on
+            done[alive] += n_com
+            seq_steps += B
+            raw += int(n_com.sum())
+            keep = done[alive] < target
+            rows += T
+            steps += 1
+            if not keep.all():
+                idx = torch.from_numpy(np.repeat(np.nonzero(keep)[0] * (K + 1), K + 1)
+                                       + np.tile(np.arange(K + 1), int(keep.sum()))).cuda()
+                h_out = h_out.index_select(0, idx) if idx.numel() else h_out[:0]
+                alive = alive[keep]
+            h_in = h_out
+        return recorded, steps, rows, int(np.minimum(done, target).sum()), raw / seq_steps
+
+    print(f"[bench] rehearsing the loop (K={K}, p={p})", file=sys.stderr, flush=True)
+    plan, steps, rows, committed, per_seq_step = loop()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, steps2, _, committed2, _ = loop(plan)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert steps2 == steps and committed2 == committed
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+
+        T0 = B0 * (K + 1)
+        dr = bd.to_host(plan[0])
+        t1 = time.perf_counter()
+        r = O.verify_step(h_np[:T0], dr, W, dims)
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(float(np.sum(r["n_committed"])) / dt, 3), "unit": "committed tokens/s",
+               "cores": _cores(), "kind": "oracle",
+               "sample": f"the loop's first verify step ({B0} sequences, K={K}); float64 numpy oracle",
+               "s_per_step": round(dt, 3)}
+    line = {"metric": METRIC, "value": round(committed / wall, 1), "unit": "committed tokens/s"}
+    line.update(_header(args, wl))
+    line.update({
+        "steps": steps, "warmup": 1, "ms_per_step": round(wall / steps * 1e3, 4),
+        "scaling": "strong",
+        "data": "synthetic (seeded; weights N(0,0.02), Zipf router bias, drafts = argmax w.p. p)",
+        "config": {"workload": wl.name, "sequences": B0, "k_draft": K, "match_p": p,
+                   "tokens_per_sequence": target, "verify_steps": steps, "rows_verified": rows,
+                   "committed": int(committed), "committed_per_seq_step": round(per_seq_step, 4)},
+        "roofline": None,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 4),
+    })
+    return line
 
 
 def cpu_baseline(wl, W, h_np, drafts_np, steps):
     """The CPU oracle timed on a bounded sample of the same workload."""
     from oracle import moe_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = _cores()
     t0 = time.perf_counter()
     committed = 0
     for _ in range(steps):

@@ -21,16 +21,22 @@ int fail(int code, const char *msg) {
 }
 
 constexpr int kMaxTokens = 65535;
+// Up to this many rows the routing kernel takes one token per block.
+constexpr int kOneTokenRouteT = 256;
 constexpr int kMaxK = 15;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Upper bound of the number of 16-row expert tiles for T tokens.
-int max_tiles(const mv_config &c, int T) {
+// Rows per expert tile for a batch of T rows.
+int tile_rows(int T) { return T <= mv::kMidMinT ? mv::kTileM : mv::kMidRows; }
+
+// Upper bound of the number of expert tiles of tm rows for T tokens.
+int max_tiles(const mv_config &c, int T, int tm) {
   const int pairs = T * c.top_k;
   const int busy = pairs < c.n_routed ? pairs : c.n_routed;
-  return (pairs + (mv::kTileM - 1) * busy) / mv::kTileM + c.n_shared * ((T + mv::kTileM - 1) / mv::kTileM);
+  return (pairs + (tm - 1) * busy) / tm + c.n_shared * ((T + tm - 1) / tm);
 }
+int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(T)); }
 
 struct Layout {
   size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, arrive, total;
@@ -53,7 +59,8 @@ Layout layout(const mv_config &c, int T) {
   L.gates = take(static_cast<size_t>(T) * c.top_k * 4);
   L.seg = take(ne * 4);
   L.tiles = take(ne * 4);
-  L.tinfo = take(static_cast<size_t>(max_tiles(c, T)) * 16);
+  // sized for the smallest tiles so that the workspace grows with T
+  L.tinfo = take(static_cast<size_t>(max_tiles(c, T, mv::kTileM)) * 16);
   L.rows = take(static_cast<size_t>(T) * nslot * 4);
   L.a = take(static_cast<size_t>(T) * nslot * c.d_ff * es);
   L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
@@ -153,6 +160,7 @@ struct Step {
     a.k = c.top_k;
     a.nslot = c.top_k + c.n_shared;
     a.mode = mode;
+    a.tile_m = tile_rows(T);
     a.eps = c.rms_eps;
     a.x_out = ws + L.x;
     a.seg = seg();
@@ -174,6 +182,7 @@ struct Step {
   }
 
   bool small() const { return T <= mv::kSmallT; }
+  bool mid() const { return T > mv::kMidMinT; }
 
   // One routing launch (+ the grouping kernel on the large-batch path).
   // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
@@ -186,7 +195,8 @@ struct Step {
     cb.h_dst = h_dst;
     cb.slots = slots_in;
     cb.y_moe = y_moe;
-    int rc = hip_status(mv::launch_route(c.dtype, a, cb, small() ? 1 : mv::kTileM, s));
+    const int ntok = T <= kOneTokenRouteT ? 1 : mv::kTileM;
+    int rc = hip_status(mv::launch_route(c.dtype, a, cb, ntok, s));
     if (rc || mode != mv::kRoute || small()) return rc;
     return hip_status(mv::launch_permute(a, s));
   }
@@ -220,11 +230,11 @@ struct Step {
     const int mt = max_tiles(c, T);
     e.w_routed = lp.gu;
     e.w_shared = lp.sgu;
-    int rc = hip_status(mv::launch_gate_up(c.dtype, e, mt, s));
+    int rc = hip_status(mid() ? mv::launch_gate_up_mid(c.dtype, e, mt, s) : mv::launch_gate_up(c.dtype, e, mt, s));
     if (rc) return rc;
     e.w_routed = lp.down;
     e.w_shared = lp.sdown;
-    return hip_status(mv::launch_down(c.dtype, e, mt, s));
+    return hip_status(mid() ? mv::launch_down_mid(c.dtype, e, mt, s) : mv::launch_down(c.dtype, e, mt, s));
   }
 };
 

@@ -66,7 +66,7 @@ __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b,
 
 // Grouping of a small batch, built in LDS by every gate/up block.
 struct Grouping {
-  int cnt[kWave], run[kWave];
+  int cnt[kThreads], run[kThreads];
   int seg[kMaxExperts + 1];
   int tile_start[kMaxExperts + 1];
   int rows[kSmallT * kMaxSlots];
@@ -85,7 +85,7 @@ __device__ bool block_tile(const ExpertArgs &p, int tile, TileInfo &ti, Grouping
     return true;
   }
   const GroupOut lds{g.seg, g.tile_start, g.rows, nullptr};
-  group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds, g.cnt, g.run);
+  group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds, g.cnt, g.run, kThreads / kWave);
   __syncthreads();
   if (write_global) {  // the grouping of record, for the down kernel
     for (int i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero_cnt[i] = 0u;
@@ -210,6 +210,134 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
   }
 }
 
+// ------------------------------------------------------------ medium batches
+//
+// Tiles of up to MT * 16 rows of one expert and one wavefront per 16 output
+// columns, with no LDS: each wavefront reads its A fragments from global
+// memory (they stay in L2) next to its weight stream, so every weight row is
+// read once per tile instead of once per 16 rows.  Loads run one batch of
+// kMidWin windows ahead of the MFMAs.  Per-row arithmetic is the 16-row
+// kernels': gate and up each one MFMA chain over K in window order; down two
+// chains over the K halves, added low half first.
+constexpr int kMidWin = 2;
+
+// acc[c][i] += A_i * B_c over windows [w_lo, w_hi) for NB weight streams.
+template <typename T, int MT, int NB>
+__device__ __forceinline__ void mid_chain(f32x4_t (*acc)[MT], const T *const *ar, const T *const *b,
+                                          int w_lo, int w_hi) {
+  constexpr int WIN = 4 * Vec<T>::N, U = kMidWin;
+  uint4 qb[2][NB][U], qa[2][MT][U];
+  auto load = [&](int buf, int w0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = min(w0 + u, w_hi - 1);
+#pragma unroll
+      for (int c = 0; c < NB; ++c) qb[buf][c][u] = ld16(b[c] + w * WIN);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) qa[buf][i][u] = ld16(ar[i] + w * WIN);
+    }
+  };
+  if (w_lo >= w_hi) return;
+  load(0, w_lo);
+  int buf = 0;
+  for (int w0 = w_lo; w0 < w_hi; w0 += U, buf ^= 1) {
+    if (w0 + U < w_hi) load(buf ^ 1, w0 + U);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (w0 + u < w_hi) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int c = 0; c < NB; ++c) mfma16(acc[c][i], qa[buf][i][u], qb[buf][c][u], T());
+      }
+  }
+}
+
+template <typename T, int MT>
+__global__ __launch_bounds__(kThreads) void k_gate_up_mid(ExpertArgs p) {
+  constexpr int VN = Vec<T>::N, WIN = 4 * VN;
+  if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
+  const int4 tv = p.tile_info[blockIdx.y];
+  const int e = tv.x, r0 = tv.y, m = tv.z;
+  const int d = p.d, F = p.F;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int f0 = (blockIdx.x * (kThreads / kWave) + wv) * 16;
+  if (f0 >= F) return;  // no block-wide synchronisation below
+  const int r = lane & 15, koff = (lane >> 4) * VN;
+  const T *W = expert_base<T>(p, e, static_cast<size_t>(2) * F * d);
+  const T *b[2] = {W + static_cast<size_t>(f0 + r) * d + koff, W + static_cast<size_t>(F + f0 + r) * d + koff};
+  const T *x = static_cast<const T *>(p.x);
+  const T *ar[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int row = i * 16 + r;
+    const int pair = p.rows[r0 + (row < m ? row : 0)];
+    ar[i] = x + static_cast<size_t>(pair / p.nslot) * d + koff;
+  }
+  f32x4_t acc[2][MT];  // [gate | up][tile]
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    acc[0][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[1][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  mid_chain<T, MT, 2>(acc, ar, b, 0, d / WIN);
+  T *aout = static_cast<T *>(p.a_out);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = i * 16 + (lane >> 4) * 4 + j;
+      if (row < m) {
+        const float gv = acc[0][i][j], uv = acc[1][i][j];
+        aout[static_cast<size_t>(r0 + row) * F + f0 + r] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
+      }
+    }
+  }
+}
+
+template <typename T, int MT>
+__global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
+  constexpr int VN = Vec<T>::N, WIN = 4 * VN;
+  if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
+  const int4 tv = p.tile_info[blockIdx.y];
+  const int e = tv.x, r0 = tv.y, m = tv.z;
+  const int d = p.d, F = p.F;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * (kThreads / kWave) + wv) * 16;
+  if (n0 >= d) return;
+  const int r = lane & 15, koff = (lane >> 4) * VN;
+  const T *b[1] = {expert_base<T>(p, e, static_cast<size_t>(d) * F) + static_cast<size_t>(n0 + r) * F + koff};
+  const T *a = static_cast<const T *>(p.a);
+  const T *ar[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int row = i * 16 + r;
+    ar[i] = a + static_cast<size_t>(r0 + (row < m ? row : 0)) * F + koff;
+  }
+  f32x4_t lo[1][MT], hi[1][MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    lo[0][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    hi[0][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int nwin = F / WIN;
+  mid_chain<T, MT, 1>(lo, ar, b, 0, nwin / 2);
+  mid_chain<T, MT, 1>(hi, ar, b, nwin / 2, nwin);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = i * 16 + (lane >> 4) * 4 + j;
+      if (row < m) {
+        const int pair = p.rows[r0 + row];
+        const int tok = pair / p.nslot, s = pair - tok * p.nslot;
+        const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
+        p.slots[static_cast<size_t>(pair) * d + n0 + r] = w * (lo[0][i][j] + hi[0][i][j]);
+      }
+    }
+  }
+}
+
 template <typename KernelT>
 void allow_lds(KernelT kernel, size_t bytes) {
   if (bytes > 48 * 1024)
@@ -244,6 +372,28 @@ hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_
     allow_lds(k_down<float>, smem);
     hipLaunchKernelGGL(k_down<float>, grid, dim3(kThreads), smem, s, a);
   }
+  return hipGetLastError();
+}
+
+}  // namespace mv
+
+namespace mv {
+
+hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  const dim3 grid((a.F + 63) / 64, max_tiles);
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_gate_up_mid<bf16_t, kMidTiles>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gate_up_mid<float, kMidTiles>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  const dim3 grid((a.d + 63) / 64, max_tiles);
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_down_mid<bf16_t, kMidTiles>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_down_mid<float, kMidTiles>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -5,7 +5,7 @@
 // block on the small-batch path (the whole block on one token's latency
 // chain), sixteen on the large-batch path (router weights shared by the
 // tile).  Large batches are then grouped by a separate kernel: a ballot-based
-// one on one wavefront for up to 1024 pairs, else a stable counting sort
+// one on one block for up to 16384 pairs, else a stable counting sort
 // (per-thread histogram over contiguous pair ranges, an exclusive scan in
 // (expert, thread) order, and a scatter that keeps ascending pair order
 // inside every expert segment).
@@ -19,7 +19,7 @@ template <typename T>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, CombineArgs c, int ntok) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last;
-  __shared__ int cnt_lds[kWave], run_lds[kWave];
+  __shared__ int cnt_lds[kRouteWaves * kWave], run_lds[kRouteWaves * kWave];
   const int t0 = blockIdx.x * ntok;
   route_block<T>(a, c, t0, min(ntok, a.T - t0), ntok, smem);
   if (!a.arrive || a.mode != kRoute) return;
@@ -31,16 +31,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, CombineArg
            gridDim.x - 1;
   }
   __syncthreads();
-  if (!last || threadIdx.x >= kWave) return;
+  if (!last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const GroupOut o{a.seg, a.tile_start, a.rows, a.tile_info};
-  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, kTileM, o, cnt_lds, run_lds);
+  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, a.tile_m, o, cnt_lds, run_lds, kRouteWaves);
 }
 
-__global__ __launch_bounds__(64) void k_group(RouteArgs a) {
-  __shared__ int cnt_lds[kWave], run_lds[kWave];
+__global__ __launch_bounds__(kRouteThreads) void k_group(RouteArgs a) {
+  __shared__ int cnt_lds[kRouteWaves * kWave], run_lds[kRouteWaves * kWave];
   const GroupOut o{a.seg, a.tile_start, a.rows, a.tile_info};
-  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, kTileM, o, cnt_lds, run_lds);
+  group_pairs(a.ids, a.T, a.E, a.S, a.k, a.nslot, a.tile_m, o, cnt_lds, run_lds, kRouteWaves);
 }
 
 __global__ __launch_bounds__(256) void k_permute_large(RouteArgs p) {
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_permute_large(RouteArgs p) {
       p.seg[e] = off;
       p.tile_start[e] = tiles;
       off += c;
-      tiles += (c + kTileM - 1) / kTileM;
+      tiles += (c + p.tile_m - 1) / p.tile_m;
     }
     segl[E + S] = off;
     p.seg[E + S] = off;
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256) void k_permute_large(RouteArgs p) {
   if (tid < E + S) {
     const int c = segl[tid + 1] - segl[tid];
     const int first = p.tile_start[tid];
-    for (int j = 0; j * kTileM < c; ++j)
-      p.tile_info[first + j] = make_int4(tid, segl[tid] + j * kTileM, min(kTileM, c - j * kTileM), 0);
+    for (int j = 0; j * p.tile_m < c; ++j)
+      p.tile_info[first + j] = make_int4(tid, segl[tid] + j * p.tile_m, min(p.tile_m, c - j * p.tile_m), 0);
   }
 }
 
@@ -128,8 +128,8 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
 }
 
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s) {
-  if (a.T * a.k <= 1024) {
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(64), 0, s, a);
+  if (a.T * a.k <= 16 * 1024) {
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(kRouteThreads), 0, s, a);
   } else {
     const size_t smem =
         256 * static_cast<size_t>(a.E + 2) * 2 + 16 + 4 * static_cast<size_t>(2 * a.E + a.S + 1);

@@ -17,6 +17,12 @@ constexpr int kSmallT = 64;
 // Up to this many rows the routing kernel's last block groups the pairs (its
 // blocks publish their routing with a device-scope release, one per token).
 constexpr int kGroupInRouteT = 16;
+// Batches of more than kMidMinT rows: expert tiles of up to kMidRows rows,
+// each weight row streamed once per tile (up to kMidMinT rows, 16-row tiles
+// with more wavefronts in flight stream faster).
+constexpr int kMidMinT = 128;
+constexpr int kMidTiles = 4;
+constexpr int kMidRows = 16 * kMidTiles;
 // Largest expert count (routed + shared) and slots per token supported.
 constexpr int kMaxExperts = 64 + 4;
 constexpr int kMaxSlots = 8 + 4;
@@ -29,6 +35,7 @@ enum RouteMode {
 
 struct RouteArgs {
   int T, d, E, S, k, nslot, mode;
+  int tile_m;               // rows per expert tile of the grouping
   float eps;
   const void *gamma;        // [d]
   void *x_out;              // [T, d]
@@ -88,6 +95,8 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_down_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t s);
 

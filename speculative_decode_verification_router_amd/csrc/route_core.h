@@ -24,6 +24,7 @@
 namespace mv {
 
 constexpr int kRouteThreads = 1024;  // 16 wavefronts: wavefront w owns experts 4w..4w+3
+constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouterChunks = 10;    // router chunks per lane held in registers (d <= 1280 bf16)
 
 // Router weights of one wavefront's four experts (e = e_base + (lane >> 4)):
@@ -230,74 +231,94 @@ __device__ __forceinline__ uint64_t match_lanes(int v, bool valid) {
   return valid ? m : 0ull;
 }
 
-// Stable grouping of the T*k routed pairs by expert on one wavefront, 64
-// pairs at a time: a pair's same-expert lanes give its rank among the
-// earlier pairs of its expert and, for the first of them, the count.
-// Shared expert s gets segment E + s holding every token.  Requires E <= 64
-// and `cnt_lds`, `run_lds` (LDS, >= 64 ints each).  `ids` and every output
-// may be in global memory or in LDS.
+// Stable grouping of the T*k routed pairs by expert with the block's first
+// `nw` wavefronts, each taking a contiguous run of pairs 64 at a time: a
+// pair's same-expert lanes give its rank among the earlier pairs of its
+// expert in the run and, for the first of them, the run's count; per-expert
+// offsets of the runs follow in wavefront order, so every expert segment
+// keeps ascending pair order.  Shared expert s gets segment E + s holding
+// every token.  Every thread of the block must call this (it synchronises
+// the block).  Requires E <= 64, nw * 64 <= blockDim.x and `cnt_lds`,
+// `run_lds` in LDS with nw * 64 ints each.  `ids` and every output may be in
+// global memory or in LDS.
 __device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, int nslot, int tile_m,
-                                   const GroupOut &o, int *cnt_lds, int *run_lds) {
-  if (threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
+                                   const GroupOut &o, int *cnt_lds, int *run_lds, int nw) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int np = T * k;
+  nw = max(1, min(nw, (np + kWave - 1) / kWave));  // no idle runs for small batches
+  const bool mine = w < nw;
+  const int per = ((np + nw - 1) / nw + kWave - 1) / kWave * kWave;
+  const int p0 = mine ? min(np, w * per) : 0, p1 = mine ? min(np, p0 + per) : 0;
   const uint64_t below = (1ull << lane) - 1ull;
-  cnt_lds[lane] = 0;
-  run_lds[lane] = 0;
-  __builtin_amdgcn_wave_barrier();
-  for (int base = 0; base < np; base += kWave) {
+  if (mine) cnt_lds[w * kWave + lane] = 0;
+  __syncthreads();
+  for (int base = p0; base < p1; base += kWave) {
     const int q = base + lane;
-    const int e_q = q < np ? ids[q] : 0;
-    const uint64_t m = match_lanes(e_q, q < np);
-    if (q < np && (m & below) == 0) cnt_lds[e_q] += __popcll(m);  // first lane of its expert
+    const int e_q = q < p1 ? ids[q] : 0;
+    const uint64_t m = match_lanes(e_q, q < p1);
+    if (q < p1 && (m & below) == 0) cnt_lds[w * kWave + e_q] += __popcll(m);  // first lane of its expert
     __builtin_amdgcn_wave_barrier();
   }
-  // exclusive scans over the experts (lanes) of counts and tile counts
-  const int cnt = lane < E ? cnt_lds[lane] : 0;
-  const int tiles = (cnt + tile_m - 1) / tile_m;
-  int sc = cnt, st = tiles;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int vc = __shfl_up(sc, off), vt = __shfl_up(st, off);
-    if (lane >= off) { sc += vc; st += vt; }
-  }
-  const int seg_e = sc - cnt, tile_e = st - tiles;
-  const int routed_total = __builtin_amdgcn_readlane(sc, kWave - 1);
-  const int routed_tiles = __builtin_amdgcn_readlane(st, kWave - 1);
-  if (lane < E) {
-    o.seg[lane] = seg_e;
-    o.tile_start[lane] = tile_e;
-  }
+  __syncthreads();
   const int shared_tiles = (T + tile_m - 1) / tile_m;
-  if (lane <= S) {
-    o.seg[E + lane] = routed_total + lane * T;
-    o.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
+  __shared__ int routed_end[2];
+  if (w == 0) {
+    // per expert (lane): offsets of the runs, then scans over the experts
+    int cnt = 0;
+    for (int v = 0; v < nw; ++v) {
+      const int c = lane < E ? cnt_lds[v * kWave + lane] : 0;
+      run_lds[v * kWave + lane] = cnt;
+      cnt += c;
+    }
+    const int tiles = (cnt + tile_m - 1) / tile_m;
+    int sc = cnt, st = tiles;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int vc = __shfl_up(sc, off), vt = __shfl_up(st, off);
+      if (lane >= off) { sc += vc; st += vt; }
+    }
+    const int seg_e = sc - cnt, tile_e = st - tiles;
+    const int routed_total = __builtin_amdgcn_readlane(sc, kWave - 1);
+    const int routed_tiles = __builtin_amdgcn_readlane(st, kWave - 1);
+    if (lane < E) {
+      o.seg[lane] = seg_e;
+      o.tile_start[lane] = tile_e;
+    }
+    if (lane <= S) {
+      o.seg[E + lane] = routed_total + lane * T;
+      o.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
+    }
+    for (int v = 0; v < nw; ++v) run_lds[v * kWave + lane] += seg_e;  // next free row per run
+    if (o.tile_info && lane < E)
+      for (int j = 0; j < tiles; ++j)
+        o.tile_info[tile_e + j] = make_int4(lane, seg_e + j * tile_m, min(tile_m, cnt - j * tile_m), 0);
+    if (lane == 0) {
+      routed_end[0] = routed_total;
+      routed_end[1] = routed_tiles;
+    }
   }
-  run_lds[lane] = seg_e;  // next free row of expert `lane`
-  __builtin_amdgcn_wave_barrier();
-  // scatter routed pairs, ascending pair order inside each expert
-  for (int base = 0; base < np; base += kWave) {
+  __syncthreads();
+  // scatter the routed pairs
+  for (int base = p0; base < p1; base += kWave) {
     const int q = base + lane;
-    const int e_q = q < np ? ids[q] : 0;
-    const uint64_t m = match_lanes(e_q, q < np);
-    if (q < np) o.rows[run_lds[e_q] + __popcll(m & below)] = (q / k) * nslot + (q % k);
+    const int e_q = q < p1 ? ids[q] : 0;
+    const uint64_t m = match_lanes(e_q, q < p1);
+    if (q < p1) o.rows[run_lds[w * kWave + e_q] + __popcll(m & below)] = (q / k) * nslot + (q % k);
     __builtin_amdgcn_wave_barrier();
-    if (q < np && (m & below) == 0) run_lds[e_q] += __popcll(m);
+    if (q < p1 && (m & below) == 0) run_lds[w * kWave + e_q] += __popcll(m);
     __builtin_amdgcn_wave_barrier();
   }
-  for (int j = lane; j < S * T; j += kWave) {
+  const int routed_total = routed_end[0], routed_tiles = routed_end[1];
+  for (int j = threadIdx.x; j < S * T; j += blockDim.x) {
     const int s = j / T, t = j % T;
     o.rows[routed_total + s * T + t] = t * nslot + k + s;
   }
-  if (o.tile_info) {
-    if (lane < E)
-      for (int j = 0; j < tiles; ++j)
-        o.tile_info[tile_e + j] = make_int4(lane, seg_e + j * tile_m, min(tile_m, cnt - j * tile_m), 0);
-    for (int s = 0; s < S; ++s)
-      for (int j = lane; j < shared_tiles; j += kWave)
-        o.tile_info[routed_tiles + s * shared_tiles + j] =
-            make_int4(E + s, routed_total + s * T + j * tile_m, min(tile_m, T - j * tile_m), 0);
-  }
+  if (o.tile_info)
+    for (int j = threadIdx.x; j < S * shared_tiles; j += blockDim.x) {
+      const int s = j / shared_tiles, i = j % shared_tiles;
+      o.tile_info[routed_tiles + j] =
+          make_int4(E + s, routed_total + s * T + i * tile_m, min(tile_m, T - i * tile_m), 0);
+    }
 }
 
 }  // namespace mv

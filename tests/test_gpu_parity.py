@@ -120,7 +120,7 @@ def test_layer_forward_tiny_fp32(bd, torch_cuda, tiny, T):
     _layer_check(bd, torch_cuda, dims, W, model, 0, h, f"tiny T={T}")
 
 
-@pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5)])
+@pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5), (200, 3)])
 def test_layer_forward_bf16_full_width(bd, torch_cuda, big, T, layer):
     dims, W, model = big
     h = synth.make_hidden(dims, T, seed=200 + T)
@@ -273,22 +273,27 @@ def test_deterministic_and_batch_invariant(bd, torch_cuda, big):
 
 
 @pytest.mark.parametrize("model_name", ["tiny", "big"])
-def test_same_results_on_both_batch_paths(bd, torch_cuda, tiny, big, model_name):
-    """Up to 64 rows use the single-block routing path with the combine fused
-    into the down kernel; more rows use tiled routing kernels.  Both do the
-    same arithmetic in the same order, so a sequence's results are
-    bit-identical whichever path its batch takes."""
+def test_same_results_on_every_batch_path(bd, torch_cuda, tiny, big, model_name):
+    """Batches of up to 64 rows group the pairs inside the expert kernels,
+    up to 128 rows in a grouping kernel, and larger batches use 64-row expert
+    tiles.  All paths do the same per-row arithmetic in the same order, so a
+    sequence's results are bit-identical whichever path its batch takes."""
     dims, W, model = tiny if model_name == "tiny" else big
     K = 3
-    h = synth.make_hidden(dims, 17 * (K + 1), seed=91)
-    drafts = np.random.default_rng(2).integers(0, dims.vocab, (17, K)).astype(np.int32)
-    small = bd.run_verify_step(model, _dev(bd, h[:64]), _dev(bd, drafts[:16]), 16, K, routing=True)
-    large = bd.run_verify_step(model, _dev(bd, h), _dev(bd, drafts), 17, K, routing=True)
+    n_seq = 33
+    h = synth.make_hidden(dims, n_seq * (K + 1), seed=91)
+    drafts = np.random.default_rng(2).integers(0, dims.vocab, (n_seq, K)).astype(np.int32)
+    runs = {B: bd.run_verify_step(model, _dev(bd, h[:B * (K + 1)]), _dev(bd, drafts[:B]), B, K,
+                                  routing=True)
+            for B in (16, 17, 33)}
     _sync(torch_cuda)
-    for key in ("h_out", "argmax", "committed", "n_committed"):
-        assert np.array_equal(_host(bd, small[key]), _host(bd, large[key])[:16 if key in (
-            "committed", "n_committed") else 64]), key
-    assert np.array_equal(_host(bd, small["topk_ids"]), _host(bd, large["topk_ids"])[:, :64])
+    small = runs[16]
+    for B in (17, 33):
+        other = runs[B]
+        for key in ("h_out", "argmax", "committed", "n_committed"):
+            n = 16 if key in ("committed", "n_committed") else 64
+            assert np.array_equal(_host(bd, small[key]), _host(bd, other[key])[:n]), (B, key)
+        assert np.array_equal(_host(bd, small["topk_ids"]), _host(bd, other["topk_ids"])[:, :64]), B
 
 
 def test_lossless_gpu_decode_loop(bd, torch_cuda, tiny):
