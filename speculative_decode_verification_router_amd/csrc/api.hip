@@ -27,8 +27,24 @@ constexpr int kMaxK = 15;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Rows per expert tile for a batch of T rows.
-int tile_rows(int T) { return T <= mv::kMidMinT ? mv::kTileM : mv::kMidRows; }
+// Expert-kernel family for a batch of T rows: 16-row tiles streaming the
+// weights (up to kMidMinT rows), 64-row tiles (up to kLargeMinT rows, or
+// fp32), and the LDS-tiled GEMMs of 256-row tiles (bf16 above kLargeMinT).
+enum Path { kSmallTiles, kMidTiles, kGemmTiles };
+Path path_for(const mv_config &c, int T) {
+  if (T <= mv::kMidMinT) return kSmallTiles;
+  if (c.dtype == MV_BF16 && T > mv::kLargeMinT && c.d_model % 256 == 0 && c.d_ff % 128 == 0 &&
+      c.n_shared <= 2)
+    return kGemmTiles;
+  return kMidTiles;
+}
+int tile_rows(const mv_config &c, int T) {
+  switch (path_for(c, T)) {
+    case kSmallTiles: return mv::kTileM;
+    case kMidTiles: return mv::kMidRows;
+    default: return mv::gemm_tile_rows();
+  }
+}
 
 // Upper bound of the number of expert tiles of tm rows for T tokens.
 int max_tiles(const mv_config &c, int T, int tm) {
@@ -36,10 +52,10 @@ int max_tiles(const mv_config &c, int T, int tm) {
   const int busy = pairs < c.n_routed ? pairs : c.n_routed;
   return (pairs + (tm - 1) * busy) / tm + c.n_shared * ((T + tm - 1) / tm);
 }
-int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(T)); }
+int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T)); }
 
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, arrive, total;
+  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, arrive, bcnt, total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -66,6 +82,7 @@ Layout layout(const mv_config &c, int T) {
   L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
   L.argkey = take(static_cast<size_t>(T) * 8);
   L.arrive = take(static_cast<size_t>(c.n_layers) * 4);
+  L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
   L.total = off;
   return L;
 }
@@ -160,7 +177,7 @@ struct Step {
     a.k = c.top_k;
     a.nslot = c.top_k + c.n_shared;
     a.mode = mode;
-    a.tile_m = tile_rows(T);
+    a.tile_m = tile_rows(c, T);
     a.eps = c.rms_eps;
     a.x_out = ws + L.x;
     a.seg = seg();
@@ -182,13 +199,17 @@ struct Step {
   }
 
   bool small() const { return T <= mv::kSmallT; }
-  bool mid() const { return T > mv::kMidMinT; }
+  // LDS-tiled GEMMs; the combine is in the shared experts' down projection
+  bool gemm() const { return path_for(c, T) == kGemmTiles; }
 
   // One routing launch (+ the grouping kernel on the large-batch path).
   // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
   int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
             float *y_moe, int *ids, float *gates_out, bool step = false) const {
     mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
+    if (mode == mv::kRoute && gemm()) {  // h_src is already combined on this path
+      return hip_status(mv::launch_route_large(a, h_src, reinterpret_cast<int *>(ws + L.bcnt), s));
+    }
     if (mode == mv::kRoute && group_in_route(layer, step)) a.arrive = arrive() + layer;
     mv::CombineArgs cb{};
     cb.h_src = h_src;
@@ -201,8 +222,10 @@ struct Step {
     return hip_status(mv::launch_permute(a, s));
   }
 
-  // gate/up then down for `layer`, leaving the weighted expert outputs in slots.
-  int ffn(int layer, const int *ids_in, const float *gates_in, bool step = false) const {
+  // gate/up then down for `layer`, leaving the weighted expert outputs in
+  // slots; on the GEMM path also the combine h_dst = h_src + y (y_moe: y).
+  int ffn(int layer, const int *ids_in, const float *gates_in, bool step = false,
+          const void *h_src = nullptr, void *h_dst = nullptr, float *y_moe = nullptr) const {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e{};
     e.T = T;
@@ -230,11 +253,20 @@ struct Step {
     const int mt = max_tiles(c, T);
     e.w_routed = lp.gu;
     e.w_shared = lp.sgu;
-    int rc = hip_status(mid() ? mv::launch_gate_up_mid(c.dtype, e, mt, s) : mv::launch_gate_up(c.dtype, e, mt, s));
+    const Path path = path_for(c, T);
+    int rc = hip_status(path == kGemmTiles  ? mv::launch_gemm_gate_up(e, mt, s)
+                        : path == kMidTiles ? mv::launch_gate_up_mid(c.dtype, e, mt, s)
+                                            : mv::launch_gate_up(c.dtype, e, mt, s));
     if (rc) return rc;
     e.w_routed = lp.down;
     e.w_shared = lp.sdown;
-    return hip_status(mid() ? mv::launch_down_mid(c.dtype, e, mt, s) : mv::launch_down(c.dtype, e, mt, s));
+    if (path == kGemmTiles) {
+      if ((rc = hip_status(mv::launch_gemm_down(e, mt, s)))) return rc;
+      mv::CombineArgs cb{h_src, h_dst, slots(), y_moe};
+      return hip_status(mv::launch_gemm_down_shared(e, cb, s));
+    }
+    return hip_status(path == kMidTiles ? mv::launch_down_mid(c.dtype, e, mt, s)
+                                        : mv::launch_down(c.dtype, e, mt, s));
   }
 };
 
@@ -266,6 +298,7 @@ MV_API int moe_layer_forward(const mv_config *cfg, const mv_weights *w, int32_t 
   int *ids = topk_ids ? topk_ids : reinterpret_cast<int *>(st.ws + st.L.ids);
   float *gates = topk_w ? topk_w : st.gates();
   if ((rc = st.route(layer, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates))) return rc;
+  if (st.gemm()) return st.ffn(layer, ids, gates, false, h_in, h_out, y_moe);
   if ((rc = st.ffn(layer, ids, gates))) return rc;
   return st.route(layer, mv::kCombine, h_in, h_out, st.slots(), y_moe, nullptr, nullptr);
 }
@@ -294,9 +327,17 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
   void *hbuf = h_out ? h_out : static_cast<void *>(st.ws + st.L.hbuf);
   const int L = cfg->n_layers, k = cfg->top_k;
   float *gates = st.gates();
+  const bool gemm = st.gemm();
   for (int layer = 0; layer < L; ++layer) {
     int *ids = dbg_topk_ids ? dbg_topk_ids + static_cast<size_t>(layer) * T * k
                             : reinterpret_cast<int *>(st.ws + st.L.ids);
+    const void *src = layer == 0 ? h_in : hbuf;
+    if (gemm) {  // the layer's own combine writes hbuf
+      if ((rc = st.route(layer, mv::kRoute, src, nullptr, nullptr, nullptr, ids, gates, true)) ||
+          (rc = st.ffn(layer, ids, gates, true, src, hbuf)))
+        return rc;
+      continue;
+    }
     // layer 0 routes h_in; later layers first add the previous layer's experts
     if (layer == 0)
       rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, true);
@@ -305,9 +346,11 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
                     true);
     if (rc || (rc = st.ffn(layer, ids, gates, true))) return rc;
   }
-  if ((rc = st.route(L - 1, mv::kFinal, L == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, nullptr,
-                     nullptr)))
-    return rc;
+  if (gemm)
+    rc = st.route(L - 1, mv::kFinal, hbuf, nullptr, nullptr, nullptr, nullptr, nullptr);
+  else
+    rc = st.route(L - 1, mv::kFinal, L == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, nullptr, nullptr);
+  if (rc) return rc;
 
   mv::LmArgs la{T, cfg->d_model, cfg->vocab, st.ws + st.L.x, w->lm_head, st.argkey()};
   if ((rc = hip_status(mv::launch_lm_argmax(cfg->dtype, la, st.s)))) return rc;

@@ -1,0 +1,255 @@
+// Routing and grouping for large batches (bf16, the compute-bound path).
+//
+// k_route_large: 16 tokens per block.  RMSNorm with the canonical sum of
+// squares (route_core.h), then the router logits x W_r^T on the matrix cores
+// (v_mfma_f32_32x32x16_bf16; the products of bf16 values are exact and the
+// sums fp32, in the instruction's order, two K halves added), top-k by rank
+// as in route_core.h, and the block's per-expert pair counts.
+//
+// k_scatter: the stable grouping of the (token, slot) pairs by expert from
+// those counts.  Each block takes the same 16 tokens: the counts of the
+// blocks before it give each expert's offset, a ballot match ranks its own
+// pairs, so every expert segment keeps ascending pair order.  Block 0 also
+// writes the segment and tile tables.  Routing follows the architecture
+// paragraph of "Jina AI Releases jina-ocr-v1, a 3.4B MoE Document Parser With
+// Built-In Speculative Decoding" (ainewsfeed.tech): 64 routed experts, top-6,
+// two shared experts.
+#include "route_core.h"
+
+namespace mv {
+
+namespace {
+
+constexpr int kRLTok = 16;       // tokens per routing block
+constexpr int kRLThreads = 256;  // 4 wavefronts
+
+struct RLSmem {
+  size_t x, p, lg, inv, sel, total;
+};
+__host__ __device__ inline RLSmem rl_smem(int d) {
+  const int nvec = d / 8;
+  RLSmem s;
+  s.x = 0;                                                         // [17][d + 8] bf16: rows, then a zero row
+  s.p = s.x + static_cast<size_t>(kRLTok + 1) * (d + 8) * 2;       // [16][nvec] fp32 chunk partials
+  s.lg = s.p + static_cast<size_t>(kRLTok) * nvec * 4;             // [2][32][64] fp32 logit halves
+  s.inv = s.lg + static_cast<size_t>(2) * 32 * 64 * 4;             // [16]
+  s.sel = s.inv + kRLTok * 4;                                      // [16][8]
+  s.total = s.sel + kRLTok * 8 * 4;
+  return s;
+}
+
+__global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const bf16_t *h, int *blk_cnt) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int cnt[64];
+  const int d = a.d, nvec = d / 8, ld = d + 8;
+  const RLSmem L = rl_smem(d);
+  bf16_t *xl = reinterpret_cast<bf16_t *>(smem + L.x);
+  float *pl = reinterpret_cast<float *>(smem + L.p);
+  float *lg = reinterpret_cast<float *>(smem + L.lg);
+  float *inv = reinterpret_cast<float *>(smem + L.inv);
+  float *sel = reinterpret_cast<float *>(smem + L.sel);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int t0 = blockIdx.x * kRLTok, nt = min(kRLTok, a.T - t0);
+
+  if (tid < 64) cnt[tid] = 0;
+  // rows, chunk partial sums of squares; rows nt..16 are zero (row 16 feeds
+  // the MFMA tile's rows 16..31)
+  for (int it0 = tid; it0 < (kRLTok + 1) * nvec; it0 += 4 * kRLThreads) {
+    uint4 v[4];  // four loads in flight per thread
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int it = it0 + u * kRLThreads, r = it / nvec, ch = it - r * nvec;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (it < (kRLTok + 1) * nvec && r < nt) v[u] = ld16(h + static_cast<size_t>(t0 + r) * d + ch * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int it = it0 + u * kRLThreads, r = it / nvec, ch = it - r * nvec;
+      if (it >= (kRLTok + 1) * nvec) break;
+      if (r < nt) {
+        float f[8];
+        unpack(v[u], f, bf16_t());
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += f[i] * f[i];
+        pl[r * nvec + ch] = s;
+      }
+      st16(xl + r * ld + ch * 8, v[u]);
+    }
+  }
+  __syncthreads();
+  for (int r = wv; r < nt; r += kRLThreads / kWave) {
+    float acc = 0.f;
+    for (int ch = lane; ch < nvec; ch += kWave) acc += pl[r * nvec + ch];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) inv[r] = 1.0f / sqrtf(acc / static_cast<float>(d) + a.eps);
+  }
+  __syncthreads();
+  const bf16_t *gam = static_cast<const bf16_t *>(a.gamma);
+  bf16_t *xo = static_cast<bf16_t *>(a.x_out);
+  for (int it = tid; it < nt * nvec; it += blockDim.x) {
+    const int r = it / nvec, ch = it - r * nvec;
+    float hv[8], g[8], x[8];
+    unpack(ld16(xl + r * ld + ch * 8), hv, bf16_t());
+    unpack(ld16(gam + ch * 8), g, bf16_t());
+    const float s = inv[r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = round_to<bf16_t>((hv[i] * s) * g[i]);
+    const uint4 pk = pack(x, bf16_t());
+    st16(xl + r * ld + ch * 8, pk);
+    st16(xo + static_cast<size_t>(t0 + r) * d + ch * 8, pk);
+  }
+  __syncthreads();
+
+  // logits: wavefront w takes experts 32*(w&1) .. +31 over K half (w>>1)
+  {
+    const int nwin = d / 16, half = wv >> 1;
+    const int e = min(32 * (wv & 1) + (lane & 31), a.E - 1);
+    const bf16_t *wr = static_cast<const bf16_t *>(a.router_w) + static_cast<size_t>(e) * d + (lane >> 5) * 8;
+    const bf16_t *xr = xl + min(lane & 31, kRLTok) * ld + (lane >> 5) * 8;
+    f32x16_t acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    const int w_lo = half * nwin / 2, w_hi = (half + 1) * nwin / 2;
+    for (int w0 = w_lo; w0 < w_hi; w0 += 8) {
+      uint4 b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) b[u] = ld16(wr + min(w0 + u, w_hi - 1) * 16);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (w0 + u < w_hi) mfma32(acc, ld16(xr + (w0 + u) * 16), b[u]);
+    }
+    float *dst = lg + half * 32 * 64;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      dst[row * 64 + 32 * (wv & 1) + (lane & 31)] = acc[q];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nt * 64; i += blockDim.x) {
+    const int r = i / 64, e = i % 64;
+    const float b = (a.router_b && e < a.E) ? a.router_b[e] : 0.f;
+    lg[r * 64 + e] = (lg[r * 64 + e] + lg[32 * 64 + r * 64 + e]) + b;
+  }
+  __syncthreads();
+  for (int r = wv; r < nt; r += kRLThreads / kWave)
+    select_top_k(lg + r * 64, sel + r * 8, a.E, a.k, a.ids + (t0 + r) * a.k, a.gates + (t0 + r) * a.k);
+  __syncthreads();
+  for (int i = tid; i < nt * a.k; i += blockDim.x) atomicAdd(&cnt[a.ids[t0 * a.k + i]], 1);
+  __syncthreads();
+  if (tid < 64) blk_cnt[blockIdx.x * 64 + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(kRLThreads) void k_scatter(RouteArgs a, const int *blk_cnt, int nblk) {
+  __shared__ int part_tot[4][64], part_before[4][64];
+  __shared__ int seg_e[64], base_e[64], first_run[64];
+  __shared__ int ends[2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = a.E, S = a.S, k = a.k, T = a.T, tm = a.tile_m;
+  {  // per expert: all pairs, and pairs in the blocks before this one
+    const int e = tid & 63, part = tid >> 6;
+    const int b0 = part * nblk / 4, b1 = (part + 1) * nblk / 4;
+    int tot = 0, before = 0;
+    for (int b = b0; b < b1; b += 8) {
+      int c[8];  // eight loads in flight per thread
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? blk_cnt[(b + u) * 64 + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        tot += c[u];
+        before += b + u < static_cast<int>(blockIdx.x) ? c[u] : 0;
+      }
+    }
+    part_tot[part][e] = tot;
+    part_before[part][e] = before;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int cnt = lane < E ? part_tot[0][lane] + part_tot[1][lane] + part_tot[2][lane] + part_tot[3][lane] : 0;
+    const int before = part_before[0][lane] + part_before[1][lane] + part_before[2][lane] + part_before[3][lane];
+    const int tiles = (cnt + tm - 1) / tm;
+    int sc = cnt, st = tiles;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int vc = __shfl_up(sc, off), vt = __shfl_up(st, off);
+      if (lane >= off) { sc += vc; st += vt; }
+    }
+    const int seg = sc - cnt, tile0 = st - tiles;
+    const int routed_total = __builtin_amdgcn_readlane(sc, kWave - 1);
+    const int routed_tiles = __builtin_amdgcn_readlane(st, kWave - 1);
+    seg_e[lane] = seg;
+    base_e[lane] = seg + before;
+    if (lane == 0) {
+      ends[0] = routed_total;
+      ends[1] = routed_tiles;
+    }
+    if (blockIdx.x == 0) {
+      const int shared_tiles = (T + tm - 1) / tm;
+      if (lane < E) {
+        a.seg[lane] = seg;
+        a.tile_start[lane] = tile0;
+        for (int j = 0; j < tiles; ++j)
+          a.tile_info[tile0 + j] = make_int4(lane, seg + j * tm, min(tm, cnt - j * tm), 0);
+      }
+      if (lane <= S) {
+        a.seg[E + lane] = routed_total + lane * T;
+        a.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
+      }
+      for (int j = lane; j < S * shared_tiles; j += kWave) {
+        const int s = j / shared_tiles, i = j % shared_tiles;
+        a.tile_info[routed_tiles + j] = make_int4(E + s, routed_total + s * T + i * tm, min(tm, T - i * tm), 0);
+      }
+    }
+  }
+  __syncthreads();
+  // this block's pairs: wavefront w ranks pairs [64w, 64w + 64) of the block
+  const int t0 = blockIdx.x * kRLTok, nt = min(kRLTok, T - t0);
+  const int np = nt * k, p0 = t0 * k;
+  const int nw = (np + kWave - 1) / kWave;
+  const uint64_t below = (1ull << lane) - 1ull;
+  __shared__ int run_cnt[4][64];
+  if (wv < nw) {
+    run_cnt[wv][lane] = 0;
+    __builtin_amdgcn_wave_barrier();
+    const int q = wv * kWave + lane;
+    const int e_q = q < np ? a.ids[p0 + q] : 0;
+    const uint64_t m = match_lanes(e_q, q < np);
+    if (q < np && (m & below) == 0) run_cnt[wv][e_q] = __popcll(m);
+  }
+  __syncthreads();
+  if (wv < nw) {
+    const int q = wv * kWave + lane;
+    const int e_q = q < np ? a.ids[p0 + q] : 0;
+    const uint64_t m = match_lanes(e_q, q < np);
+    int off = base_e[e_q];
+    for (int v = 0; v < wv; ++v) off += run_cnt[v][e_q];
+    if (q < np) a.rows[off + __popcll(m & below)] = ((p0 + q) / k) * a.nslot + (p0 + q) % k;
+  }
+  const int routed_total = ends[0];
+  for (int j = tid; j < S * nt; j += blockDim.x) {
+    const int s = j / nt, t = t0 + j % nt;
+    a.rows[routed_total + s * T + t] = t * a.nslot + k + s;
+  }
+}
+
+}  // namespace
+
+int route_large_blocks(int T) { return (T + kRLTok - 1) / kRLTok; }
+
+hipError_t launch_route_large(const RouteArgs &a, const void *h, int *blk_cnt, hipStream_t s) {
+  const size_t smem = rl_smem(a.d).total;
+  if (smem > 48 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_route_large),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  const int nblk = route_large_blocks(a.T);
+  hipLaunchKernelGGL(k_route_large, dim3(nblk), dim3(kRLThreads), smem, s, a, static_cast<const bf16_t *>(h),
+                     blk_cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(kRLThreads), 0, s, a, static_cast<const int *>(blk_cnt), nblk);
+  return hipGetLastError();
+}
+
+}  // namespace mv

@@ -89,6 +89,16 @@ __device__ __forceinline__ void mfma16(f32x4_t &acc, const uint4 &a, const uint4
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// One 32x32x16 bf16 MFMA (v_mfma_f32_32x32x16_bf16): lane l supplies row
+// (l % 32) of A and column (l % 32) of B, K elements 8*(l/32) .. +7 of the
+// 16-element window; D: lane l holds column l % 32, element q at row
+// 8*(q/4) + 4*(l/32) + q%4.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void mfma32(f32x16_t &acc, const uint4 &a, const uint4 &b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);

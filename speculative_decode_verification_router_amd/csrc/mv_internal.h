@@ -21,11 +21,14 @@ constexpr int kGroupInRouteT = 16;
 // each weight row streamed once per tile (up to kMidMinT rows, 16-row tiles
 // with more wavefronts in flight stream faster).
 constexpr int kMidMinT = 128;
+// bf16 batches of more than kLargeMinT rows: LDS-tiled MFMA GEMMs.
+constexpr int kLargeMinT = 512;
 constexpr int kMidTiles = 4;
 constexpr int kMidRows = 16 * kMidTiles;
 // Largest expert count (routed + shared) and slots per token supported.
 constexpr int kMaxExperts = 64 + 4;
 constexpr int kMaxSlots = 8 + 4;
+constexpr int kMaxTopK = 8;
 
 enum RouteMode {
   kRoute = 0,    // RMSNorm -> router -> top-k (-> permutation)
@@ -97,6 +100,12 @@ hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStre
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+int gemm_tile_rows();
+hipError_t launch_gemm_gate_up(const ExpertArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_gemm_down(const ExpertArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_gemm_down_shared(const ExpertArgs &a, const CombineArgs &c, hipStream_t s);
+int route_large_blocks(int T);
+hipError_t launch_route_large(const RouteArgs &a, const void *h, int *blk_cnt, hipStream_t s);
 hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t s);
 

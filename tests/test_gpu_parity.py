@@ -103,7 +103,16 @@ def _layer_check(bd, torch, dims, W, model, layer, h, label):
     gid = _host(bd, out["topk_ids"])
     same_order = np.all(gid == ref["ids"], axis=1) & live
     if same_order.any():
-        np.testing.assert_allclose(gw[same_order], ref["gates"][same_order], rtol=1e-4, atol=1e-6)
+        # x is rounded to bf16 from fp32 on the GPU and from fp64 in the
+        # oracle; an element within fp32 noise of a rounding boundary lands
+        # one ulp apart (up to 2^-5 for |x| < 8), moving a logit by at most
+        # ulp * max|W_r| and a gate by at most twice that, relatively.  Such
+        # tokens are rare; every other gate must agree to 1e-4.
+        rel = np.abs(gw[same_order] - ref["gates"][same_order]) / ref["gates"][same_order]
+        flip_tol = 2 * 2.0 ** -5 * float(np.abs(O.widen(W["router_w"][layer], dims.dtype)).max())
+        loose = np.any(rel > 1e-4, axis=1)
+        assert loose.sum() <= max(2, 0.01 * same_order.sum()), (label, int(loose.sum()))
+        assert rel.max() <= max(1e-4, flip_tol), (label, float(rel.max()), flip_tol)
     tol = TOL[dims.dtype]
     e_y = tally.rows(f"{label} y_moe", _host(bd, out["y_moe"]), ref["y"], tol)
     e_h = tally.rows(f"{label} h_out", O.widen(_host(bd, out["h_out"]), dims.dtype),
@@ -120,7 +129,7 @@ def test_layer_forward_tiny_fp32(bd, torch_cuda, tiny, T):
     _layer_check(bd, torch_cuda, dims, W, model, 0, h, f"tiny T={T}")
 
 
-@pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5), (200, 3)])
+@pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5), (200, 3), (600, 7)])
 def test_layer_forward_bf16_full_width(bd, torch_cuda, big, T, layer):
     dims, W, model = big
     h = synth.make_hidden(dims, T, seed=200 + T)
@@ -209,6 +218,17 @@ def test_verify_c32_k3_sampled(bd, torch_cuda, big):
     h = synth.workload_hidden(wl)
     _verify_check(bd, torch_cuda, dims, W, model, h, wl.batch, wl.k_draft, wl.match_p, 0,
                   "c32_k3 verify", rows=[0, 9, 17, 31])
+
+
+@pytest.mark.timeout(600)
+def test_verify_large_batch_sampled(bd, torch_cuda, big):
+    """150 sequences x 4 rows: the LDS-tiled GEMM path with the combine in
+    the shared experts' down projection; the oracle checks sampled sequences."""
+    dims, W, model = big
+    B, K = 150, 3
+    h = synth.make_hidden(dims, B * (K + 1), seed=600)
+    _verify_check(bd, torch_cuda, dims, W, model, h, B, K, 0.6, 3, "verify B=150 K=3",
+                  rows=[0, 77, 149])
 
 
 @pytest.mark.timeout(600)
