@@ -1,0 +1,161 @@
+// Expert-tile building blocks: 256 threads (local index tid, four wavefronts)
+// work on one tile of up to 16 rows of one expert's segment of the sorted
+// pair list, streaming weight rows from HBM straight into MFMA B-operand
+// registers with 16-byte loads, eight K-windows in flight per wavefront.
+//
+//   gate/up: a slice pair is two 16-column slices of F; per slice one
+//            wavefront streams the gate rows and one the up rows over the
+//            full K = d; a = round(SiLU(g) * u) after an LDS exchange.
+//   down:    a slice pair is two 16-column slices of d; per slice two
+//            wavefronts split K = F in halves, added in a fixed order through
+//            LDS; slot[pair] = w_pair * y.
+// w_pair is the softmax gate of the routed pair, or 1 for a shared expert
+// (architecture paragraph of "Jina AI Releases jina-ocr-v1, a 3.4B MoE
+// Document Parser With Built-In Speculative Decoding", ainewsfeed.tech: two
+// shared experts beside 64 routed ones).
+#pragma once
+
+#include "route_core.h"
+
+namespace mv {
+
+constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kUnroll = 8;     // K-windows whose loads are issued together
+
+struct TileInfo {
+  int e, r0, m;
+};
+
+template <typename T>
+__device__ __forceinline__ const T *expert_base(const ExpertArgs &p, int e, size_t elems) {
+  return e < p.E ? static_cast<const T *>(p.w_routed) + static_cast<size_t>(e) * elems
+                 : static_cast<const T *>(p.w_shared) + static_cast<size_t>(e - p.E) * elems;
+}
+
+// Weight loads of windows [w0, min(w0 + kUnroll, w_hi)) into registers.
+template <typename T>
+__device__ __forceinline__ void load_batch(uint4 *q, const T *b, int w0, int w_hi) {
+  constexpr int W = 4 * Vec<T>::N;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (w0 + u < w_hi) q[u] = ld16(b + (w0 + u) * W);
+}
+
+// acc += A[16 x K] * B[K x 16] over windows [w_lo, w_hi), the first batch of
+// weights already in `q`: lane l reads A row (l % 16) from `a` (LDS) and B
+// column (l % 16) from `b` (global), both at K offset (l / 16) * VN inside
+// each window of 4*VN elements.
+template <typename T>
+__device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
+                                           uint4 *q) {
+  constexpr int W = 4 * Vec<T>::N;
+  for (int w0 = w_lo; w0 < w_hi; w0 += kUnroll) {
+    if (w0 != w_lo) load_batch<T>(q, b, w0, w_hi);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+  }
+}
+
+// The tile's a rows (zero-filled past m) into LDS, row stride F + one vector.
+template <typename T>
+__device__ __forceinline__ void stage_a_tile(const ExpertArgs &p, const TileInfo &ti, T *A, int tid, int nthreads) {
+  constexpr int VN = Vec<T>::N;
+  const int F = p.F, nvec = F / VN, lda = F + VN;
+  const T *a = static_cast<const T *>(p.a);
+  for (int it = tid; it < kTileM * nvec; it += nthreads) {
+    const int rr = it / nvec, c = it - rr * nvec;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < ti.m) v = ld16(a + static_cast<size_t>(ti.r0 + rr) * F + c * VN);
+    st16(A + rr * lda + c * VN, v);
+  }
+}
+
+// gate/up of slice pair `pair` of a tile.  begin() issues the first weight
+// batch; finish() runs the MFMAs with this lane's A row at `arow` (LDS),
+// exchanges the up accumulators and writes a (one block barrier inside).
+template <typename T>
+struct GateUpPart {
+  const T *b;
+  int f0, which, slice, nwin;
+  uint4 q[kUnroll];
+  __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid) {
+    constexpr int VN = Vec<T>::N;
+    const int lane = tid & 63, wv = tid >> 6;
+    slice = wv >> 1;
+    which = wv & 1;  // 0 gate rows, 1 up rows
+    f0 = (pair * 2 + slice) * 16;
+    const int d = p.d, F = p.F, r = lane & 15, koff = (lane >> 4) * VN;
+    nwin = f0 < F ? d / (4 * VN) : 0;
+    const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(2) * F * d);
+    b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
+    load_batch<T>(q, b, 0, nwin);
+  }
+  __device__ __forceinline__ void finish(const ExpertArgs &p, const TileInfo &ti, const T *arow,
+                                         float (*up_acc)[64][4], int tid) {
+    const int lane = tid & 63, F = p.F;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    mfma_panel<T>(acc, arow, b, 0, nwin, q);
+    if (which == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up_acc[slice][lane][i] = acc[i];
+    }
+    __syncthreads();
+    if (which == 1 || f0 >= F) return;
+    T *aout = static_cast<T *>(p.a_out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < ti.m) {
+        const float gv = acc[i], uv = up_acc[slice][lane][i];
+        aout[static_cast<size_t>(ti.r0 + row) * F + f0 + (lane & 15)] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
+      }
+    }
+  }
+};
+
+// down of slice pair `pair` of a tile; same split as GateUpPart.
+template <typename T>
+struct DownPart {
+  const T *b;
+  int n0, half, slice, w_lo, w_hi;
+  uint4 q[kUnroll];
+  __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid) {
+    constexpr int VN = Vec<T>::N;
+    const int lane = tid & 63, wv = tid >> 6;
+    slice = wv >> 1;
+    half = wv & 1;
+    n0 = (pair * 2 + slice) * 16;
+    const int d = p.d, F = p.F, r = lane & 15, koff = (lane >> 4) * VN;
+    const int nwin = F / (4 * VN);
+    w_lo = n0 < d ? half * nwin / 2 : 0;
+    w_hi = n0 < d ? (half + 1) * nwin / 2 : 0;
+    const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
+    b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
+    load_batch<T>(q, b, w_lo, w_hi);
+  }
+  __device__ __forceinline__ void finish(const ExpertArgs &p, const TileInfo &ti, const T *arow,
+                                         float (*half_acc)[64][4], int tid) {
+    const int lane = tid & 63, d = p.d;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    mfma_panel<T>(acc, arow, b, w_lo, w_hi, q);
+    if (half == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) half_acc[slice][lane][i] = acc[i];
+    }
+    __syncthreads();
+    if (half == 1 || n0 >= d) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < ti.m) {
+        const int pair = p.rows[ti.r0 + row];
+        const int tok = pair / p.nslot, s = pair - tok * p.nslot;
+        const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
+        p.slots[static_cast<size_t>(pair) * d + n0 + (lane & 15)] = w * (acc[i] + half_acc[slice][lane][i]);
+      }
+    }
+  }
+};
+
+}  // namespace mv

@@ -1,68 +1,15 @@
 // Grouped expert FFN kernels (routed experts and the always-on shared ones).
 //
-// Work is organised in tiles of up to 16 rows of one expert's segment of the
-// sorted (token, slot) pair list.  A block stages its tile's activation rows
-// in LDS (the MFMA A operand) and streams weight rows from HBM straight into
-// MFMA B-operand registers with 16-byte loads, eight K-windows in flight per
-// wavefront.
-//
-//   gate/up:  block = two 16-column slices of F; per slice one wavefront
-//             streams the gate rows and one the up rows over the full K = d;
-//             a = round(SiLU(g) * u) after an LDS exchange.
-//   down:     block = two 16-column slices of d; per slice two wavefronts
-//             split K = F in halves, added in a fixed order through LDS;
-//             slot[pair] = w_pair * y.
-// w_pair is the softmax gate of the routed pair, or 1 for a shared expert
-// (architecture paragraph of "Jina AI Releases jina-ocr-v1, a 3.4B MoE
-// Document Parser With Built-In Speculative Decoding", ainewsfeed.tech: two
-// shared experts beside 64 routed ones).
-//
-// Small batches skip the separate grouping kernel: every gate/up block groups
+// Up to 128 rows a block is one 16-row tile and one slice pair (the tile
+// parts of expert_core.h), with the tile's activation rows staged in LDS as
+// the MFMA A operand.  Small batches skip the separate grouping kernel: every gate/up block groups
 // the T*k routed pairs itself (one wavefront, a few ballots per expert) and
 // block (0, 0) also writes the grouping for the down kernel.
-#include "route_core.h"
+#include "expert_core.h"
 
 namespace mv {
 
 namespace {
-
-constexpr int kThreads = 256;  // 4 wavefronts
-constexpr int kUnroll = 8;     // K-windows whose loads are issued together
-
-struct TileInfo {
-  int e, r0, m;
-};
-
-template <typename T>
-__device__ __forceinline__ const T *expert_base(const ExpertArgs &p, int e, size_t elems) {
-  return e < p.E ? static_cast<const T *>(p.w_routed) + static_cast<size_t>(e) * elems
-                 : static_cast<const T *>(p.w_shared) + static_cast<size_t>(e - p.E) * elems;
-}
-
-// Weight loads of windows [w0, min(w0 + kUnroll, w_hi)) into registers.
-template <typename T>
-__device__ __forceinline__ void load_batch(uint4 *q, const T *b, int w0, int w_hi) {
-  constexpr int W = 4 * Vec<T>::N;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
-    if (w0 + u < w_hi) q[u] = ld16(b + (w0 + u) * W);
-}
-
-// acc += A[16 x K] * B[K x 16] over windows [w_lo, w_hi), the first batch of
-// weights already in `q`: lane l reads A row (l % 16) from `a` (LDS) and B
-// column (l % 16) from `b` (global), both at K offset (l / 16) * VN inside
-// each window of 4*VN elements.
-template <typename T>
-__device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
-                                           uint4 *q) {
-  constexpr int W = 4 * Vec<T>::N;
-  for (int w0 = w_lo; w0 < w_hi; w0 += kUnroll) {
-    if (w0 != w_lo) load_batch<T>(q, b, w0, w_hi);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
-  }
-}
 
 // Grouping of a small batch, built in LDS by every gate/up block.
 struct Grouping {
@@ -119,17 +66,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   TileInfo ti;
   if (!block_tile(p, blockIdx.y, ti, g, p.group_in_block && blockIdx.x == 0 && blockIdx.y == 0))
     return;
-  const int d = p.d, F = p.F, nvec = d / VN, lda = d + VN;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int slice = wv >> 1, which = wv & 1;  // which: 0 gate rows, 1 up rows
-  const int f0 = (blockIdx.x * 2 + slice) * 16;
-  const int r = lane & 15, koff = (lane >> 4) * VN;
-  const int nwin = f0 < F ? d / (4 * VN) : 0;
-  const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(2) * F * d);
-  const T *b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
-  uint4 q[kUnroll];
-  load_batch<T>(q, b, 0, nwin);  // first weights in flight while x is staged
+  GateUpPart<T> part;
+  part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while x is staged
 
+  const int d = p.d, nvec = d / VN, lda = d + VN;
   const int *rows = p.group_in_block ? g.rows : p.rows;
   T *A = reinterpret_cast<T *>(smem);
   const T *x = static_cast<const T *>(p.x);
@@ -140,24 +80,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
     st16(A + rr * lda + c * VN, v);
   }
   __syncthreads();
-
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  mfma_panel<T>(acc, A + r * lda + koff, b, 0, nwin, q);
-  if (which == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) up_acc[slice][lane][i] = acc[i];
-  }
-  __syncthreads();
-  if (which == 1 || f0 >= F) return;
-  T *aout = static_cast<T *>(p.a_out);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (lane >> 4) * 4 + i;
-    if (row < ti.m) {
-      const float gv = acc[i], uv = up_acc[slice][lane][i];
-      aout[static_cast<size_t>(ti.r0 + row) * F + f0 + r] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
-    }
-  }
+  const int lane = threadIdx.x & 63;
+  part.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, up_acc, threadIdx.x);
 }
 
 template <typename T>
@@ -168,46 +92,13 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
   if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
   const int4 tv = p.tile_info[blockIdx.y];
   const TileInfo ti{tv.x, tv.y, tv.z};
-  const int d = p.d, F = p.F, nvec = F / VN, lda = F + VN;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int slice = wv >> 1, half = wv & 1;
-  const int n0 = (blockIdx.x * 2 + slice) * 16;
-  const int r = lane & 15, koff = (lane >> 4) * VN;
-  const int nwin = F / (4 * VN);
-  const int w_lo = n0 < d ? half * nwin / 2 : 0, w_hi = n0 < d ? (half + 1) * nwin / 2 : 0;
-  const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
-  const T *b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
-  uint4 q[kUnroll];
-  load_batch<T>(q, b, w_lo, w_hi);  // first weights in flight while a is staged
-
-  T *A = reinterpret_cast<T *>(smem);
-  const T *a = static_cast<const T *>(p.a);
-  for (int it = threadIdx.x; it < kTileM * nvec; it += blockDim.x) {
-    const int rr = it / nvec, c = it - rr * nvec;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < ti.m) v = ld16(a + static_cast<size_t>(ti.r0 + rr) * F + c * VN);
-    st16(A + rr * lda + c * VN, v);
-  }
+  DownPart<T> part;
+  part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while a is staged
+  stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
   __syncthreads();
-
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  mfma_panel<T>(acc, A + r * lda + koff, b, w_lo, w_hi, q);
-  if (half == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) half_acc[slice][lane][i] = acc[i];
-  }
-  __syncthreads();
-  if (half == 1 || n0 >= d) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (lane >> 4) * 4 + i;
-    if (row < ti.m) {
-      const int pair = p.rows[ti.r0 + row];
-      const int tok = pair / p.nslot, s = pair - tok * p.nslot;
-      const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
-      p.slots[static_cast<size_t>(pair) * d + n0 + r] = w * (acc[i] + half_acc[slice][lane][i]);
-    }
-  }
+  const int lane = threadIdx.x & 63;
+  part.finish(p, ti, reinterpret_cast<const T *>(smem) + (lane & 15) * (p.F + VN) + (lane >> 4) * VN, half_acc,
+              threadIdx.x);
 }
 
 // ------------------------------------------------------------ medium batches

@@ -8,21 +8,16 @@
 // running (value, id) maximum per token packed into a 64-bit key that orders
 // by value and then by lower id, and one 64-bit atomicMax per token and block
 // folds the blocks together; the result does not depend on block order.
-#include "mv_common.h"
-#include "mv_internal.h"
+#include "lm_core.h"
 
 namespace mv {
 
 namespace {
 
-constexpr int kLmWaves = 4;
-constexpr int kLmSlices = 4;   // 16-row vocabulary slices per wavefront
-constexpr int kLmUnroll = 8;
-
 template <typename T>
 __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int VN = Vec<T>::N, WIN = 4 * VN;
+  constexpr int VN = Vec<T>::N;
   const int r0 = blockIdx.y * kTileM;
   const int m = min(kTileM, p.T - r0);
   const int d = p.d, nvec = d / VN, lda = d + VN;
@@ -37,56 +32,7 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
     st16(A + r * lda + c * VN, v);
   }
   __syncthreads();
-
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int koff = (lane >> 4) * VN;
-  const T *ar = A + (lane & 15) * lda + koff;
-  const int nwin = d / WIN;
-  uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
-  const int vbase = (blockIdx.x * kLmWaves + wv) * 16 * kLmSlices;
-  for (int sl = 0; sl < kLmSlices; ++sl) {
-    const int v0 = vbase + sl * 16;
-    if (v0 >= p.V) break;
-    const int v = v0 + (lane & 15);
-    const T *b = static_cast<const T *>(p.w) + static_cast<size_t>(min(v, p.V - 1)) * d + koff;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int w0 = 0; w0 < nwin; w0 += kLmUnroll) {
-      uint4 q[kLmUnroll];
-#pragma unroll
-      for (int u = 0; u < kLmUnroll; ++u)
-        if (w0 + u < nwin) q[u] = ld16(b + (w0 + u) * WIN);
-#pragma unroll
-      for (int u = 0; u < kLmUnroll; ++u)
-        if (w0 + u < nwin) mfma16(acc, ld16(ar + (w0 + u) * WIN), q[u], T());
-    }
-    if (v < p.V) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint64_t key = argmax_key(acc[i], static_cast<uint32_t>(v));
-        best[i] = key > best[i] ? key : best[i];
-      }
-    }
-  }
-  // maximum over the 16 lanes that share rows 4*(lane/16)..+3
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const uint64_t other = shfl_xor_u64(best[i], o);
-      best[i] = other > best[i] ? other : best[i];
-    }
-  }
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wv][(lane >> 4) * 4 + i] = best[i];
-  }
-  __syncthreads();
-  if (threadIdx.x < m) {
-    uint64_t k = 0ull;
-#pragma unroll
-    for (int w = 0; w < kLmWaves; ++w) k = red[w][threadIdx.x] > k ? red[w][threadIdx.x] : k;
-    if (k != 0ull) atomicMax(p.argkey + r0 + threadIdx.x, static_cast<unsigned long long>(k));
-  }
+  lm_rows_block<T>(p, blockIdx.x, r0, m, A, lda, red, threadIdx.x);
 }
 
 // Up to 128 rows: every block takes all rows of its 16*MT-row group, so the

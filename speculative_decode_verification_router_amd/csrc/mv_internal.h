@@ -15,7 +15,7 @@ constexpr int kTileM = 16;
 // expert itself instead of a separate grouping kernel.
 constexpr int kSmallT = 64;
 // Up to this many rows the routing kernel's last block groups the pairs (its
-// blocks publish their routing with a device-scope release, one per token).
+// blocks publish their routing with written-through stores, one per token).
 constexpr int kGroupInRouteT = 16;
 // Batches of more than kMidMinT rows: expert tiles of up to kMidRows rows,
 // each weight row streamed once per tile (up to kMidMinT rows, 16-row tiles
