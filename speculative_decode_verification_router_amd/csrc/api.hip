@@ -55,7 +55,7 @@ int max_tiles(const mv_config &c, int T, int tm) {
 int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T)); }
 
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, arrive, bcnt, total;
+  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, bcnt, total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -81,7 +81,6 @@ Layout layout(const mv_config &c, int T) {
   L.a = take(static_cast<size_t>(T) * nslot * c.d_ff * es);
   L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
   L.argkey = take(static_cast<size_t>(T) * 8);
-  L.arrive = take(static_cast<size_t>(c.n_layers) * 4);
   L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
   L.total = off;
   return L;
@@ -163,10 +162,6 @@ struct Step {
   float *slots() const { return reinterpret_cast<float *>(ws + L.slots); }
   float *gates() const { return reinterpret_cast<float *>(ws + L.gates); }
   unsigned long long *argkey() const { return reinterpret_cast<unsigned long long *>(ws + L.argkey); }
-  unsigned *arrive() const { return reinterpret_cast<unsigned *>(ws + L.arrive); }
-  // Layers >= 1 of a step with at most kGroupInRouteT rows are grouped by the
-  // routing kernel (arrival counter per layer, cleared by layer 0's gate/up).
-  bool group_in_route(int layer, bool step) const { return step && layer > 0 && T <= mv::kGroupInRouteT; }
 
   mv::RouteArgs route_args(int layer, int mode, int *ids, float *gates_out) const {
     mv::RouteArgs a{};
@@ -205,12 +200,11 @@ struct Step {
   // One routing launch (+ the grouping kernel on the large-batch path).
   // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
   int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
-            float *y_moe, int *ids, float *gates_out, bool step = false) const {
+            float *y_moe, int *ids, float *gates_out) const {
     mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
     if (mode == mv::kRoute && gemm()) {  // h_src is already combined on this path
       return hip_status(mv::launch_route_large(a, h_src, reinterpret_cast<int *>(ws + L.bcnt), s));
     }
-    if (mode == mv::kRoute && group_in_route(layer, step)) a.arrive = arrive() + layer;
     mv::CombineArgs cb{};
     cb.h_src = h_src;
     cb.h_dst = h_dst;
@@ -224,8 +218,8 @@ struct Step {
 
   // gate/up then down for `layer`, leaving the weighted expert outputs in
   // slots; on the GEMM path also the combine h_dst = h_src + y (y_moe: y).
-  int ffn(int layer, const int *ids_in, const float *gates_in, bool step = false,
-          const void *h_src = nullptr, void *h_dst = nullptr, float *y_moe = nullptr) const {
+  int ffn(int layer, const int *ids_in, const float *gates_in, const void *h_src = nullptr,
+          void *h_dst = nullptr, float *y_moe = nullptr) const {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e{};
     e.T = T;
@@ -243,11 +237,7 @@ struct Step {
     e.rows = rows();
     e.tile_info = tinfo();
     e.ids = ids_in;
-    e.group_in_block = small() && !group_in_route(layer, step) ? 1 : 0;
-    if (step && layer == 0 && T <= mv::kGroupInRouteT) {
-      e.zero_cnt = arrive();
-      e.n_zero = c.n_layers;
-    }
+    e.group_in_block = small() ? 1 : 0;
     e.gates = gates_in;
     e.slots = slots();
     const int mt = max_tiles(c, T);
@@ -298,7 +288,7 @@ MV_API int moe_layer_forward(const mv_config *cfg, const mv_weights *w, int32_t 
   int *ids = topk_ids ? topk_ids : reinterpret_cast<int *>(st.ws + st.L.ids);
   float *gates = topk_w ? topk_w : st.gates();
   if ((rc = st.route(layer, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates))) return rc;
-  if (st.gemm()) return st.ffn(layer, ids, gates, false, h_in, h_out, y_moe);
+  if (st.gemm()) return st.ffn(layer, ids, gates, h_in, h_out, y_moe);
   if ((rc = st.ffn(layer, ids, gates))) return rc;
   return st.route(layer, mv::kCombine, h_in, h_out, st.slots(), y_moe, nullptr, nullptr);
 }
@@ -333,18 +323,17 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
                             : reinterpret_cast<int *>(st.ws + st.L.ids);
     const void *src = layer == 0 ? h_in : hbuf;
     if (gemm) {  // the layer's own combine writes hbuf
-      if ((rc = st.route(layer, mv::kRoute, src, nullptr, nullptr, nullptr, ids, gates, true)) ||
-          (rc = st.ffn(layer, ids, gates, true, src, hbuf)))
+      if ((rc = st.route(layer, mv::kRoute, src, nullptr, nullptr, nullptr, ids, gates)) ||
+          (rc = st.ffn(layer, ids, gates, src, hbuf)))
         return rc;
       continue;
     }
     // layer 0 routes h_in; later layers first add the previous layer's experts
     if (layer == 0)
-      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, true);
+      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates);
     else
-      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates,
-                    true);
-    if (rc || (rc = st.ffn(layer, ids, gates, true))) return rc;
+      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates);
+    if (rc || (rc = st.ffn(layer, ids, gates))) return rc;
   }
   if (gemm)
     rc = st.route(L - 1, mv::kFinal, hbuf, nullptr, nullptr, nullptr, nullptr, nullptr);

@@ -35,7 +35,6 @@ __device__ bool block_tile(const ExpertArgs &p, int tile, TileInfo &ti, Grouping
   group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds, g.cnt, g.run, kThreads / kWave);
   __syncthreads();
   if (write_global) {  // the grouping of record, for the down kernel
-    for (int i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero_cnt[i] = 0u;
     for (int i = threadIdx.x; i <= ne; i += blockDim.x) {
       p.seg[i] = g.seg[i];
       p.tile_start[i] = g.tile_start[i];

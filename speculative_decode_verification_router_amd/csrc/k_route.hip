@@ -18,25 +18,8 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, CombineArgs c, int ntok) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int last;
-  __shared__ int cnt_lds[kRouteWaves * kWave], run_lds[kRouteWaves * kWave];
   const int t0 = blockIdx.x * ntok;
   route_block<T>(a, c, t0, min(ntok, a.T - t0), ntok, smem);
-  if (!a.arrive || a.mode != kRoute) return;
-  // Publish this block's routing, the last block to arrive groups the pairs.
-  // The ids were written through to memory (agent-scope stores); waiting for
-  // their completion before the counter update orders them before it, and
-  // the last block reads them with agent-scope loads, so no cache write-back
-  // or invalidation is needed.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(a.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           gridDim.x - 1;
-  __syncthreads();
-  if (!last) return;
-  const GroupOut o{a.seg, a.tile_start, a.rows, a.tile_info};
-  group_pairs<true>(a.ids, a.T, a.E, a.S, a.k, a.nslot, a.tile_m, o, cnt_lds, run_lds, kRouteWaves);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void k_group(RouteArgs a) {

@@ -14,9 +14,6 @@ constexpr int kTileM = 16;
 // block per token, and every gate/up block groups the (token, slot) pairs by
 // expert itself instead of a separate grouping kernel.
 constexpr int kSmallT = 64;
-// Up to this many rows the routing kernel's last block groups the pairs (its
-// blocks publish their routing with written-through stores, one per token).
-constexpr int kGroupInRouteT = 16;
 // Batches of more than kMidMinT rows: expert tiles of up to kMidRows rows,
 // each weight row streamed once per tile (up to kMidMinT rows, 16-row tiles
 // with more wavefronts in flight stream faster).
@@ -49,7 +46,6 @@ struct RouteArgs {
   int *seg, *tile_start, *rows;
   int4 *tile_info;          // [max tiles] (expert, first row, rows, 0) per 16-row tile
   unsigned long long *argkey;  // kFinal: cleared
-  unsigned *arrive;         // if set: the last block to finish groups the pairs by expert
 };
 
 // Combine of the previous layer's expert slots into the hidden state.
@@ -71,8 +67,6 @@ struct ExpertArgs {
   int group_in_block;      // small path: gate/up groups the pairs (block (0,0) writes them)
   int *seg, *tile_start, *rows;
   int4 *tile_info;         // [max tiles] (expert, first row, rows, 0)
-  unsigned *zero_cnt;      // gate/up block (0,0): clears these counters (n_zero)
-  int n_zero;
   const float *gates;      // [T, k]
   float *slots;            // [T*nslot, d]
 };

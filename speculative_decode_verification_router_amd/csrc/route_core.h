@@ -88,15 +88,14 @@ __device__ __forceinline__ void select_top_k(const float *lg_row, float *sel_lds
   const float ex = expf(logit - vmax);
   if (chosen) {
     sel_lds[rank] = ex;
-    // write-through store (agent scope): another block may group these ids
-    __hip_atomic_store(ids + rank, lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ids[rank] = lane;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float den = 0.f;
   for (int s = 0; s < k; ++s) den += sel_lds[s];
-  if (chosen) __hip_atomic_store(gates + rank, ex / den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (chosen) gates[rank] = ex / den;
 }
 
 // LDS layout of a routing block holding `ntok` token rows.
@@ -242,14 +241,8 @@ __device__ __forceinline__ uint64_t match_lanes(int v, bool valid) {
 // the block).  Requires E <= 64, nw * 64 <= blockDim.x and `cnt_lds`,
 // `run_lds` in LDS with nw * 64 ints each.  `ids` and every output may be in
 // global memory or in LDS.
-// With kCoherent the ids are read with agent-scope loads that bypass stale
-// L2 lines (ids published by other blocks of the same kernel).
-template <bool kCoherent = false>
 __device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, int nslot, int tile_m,
                                    const GroupOut &o, int *cnt_lds, int *run_lds, int nw) {
-  auto id_at = [&](int q) {
-    return kCoherent ? __hip_atomic_load(ids + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ids[q];
-  };
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int np = T * k;
   nw = max(1, min(nw, (np + kWave - 1) / kWave));  // no idle runs for small batches
@@ -261,7 +254,7 @@ __device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, i
   __syncthreads();
   for (int base = p0; base < p1; base += kWave) {
     const int q = base + lane;
-    const int e_q = q < p1 ? id_at(q) : 0;
+    const int e_q = q < p1 ? ids[q] : 0;
     const uint64_t m = match_lanes(e_q, q < p1);
     if (q < p1 && (m & below) == 0) cnt_lds[w * kWave + e_q] += __popcll(m);  // first lane of its expert
     __builtin_amdgcn_wave_barrier();
@@ -308,7 +301,7 @@ __device__ inline void group_pairs(const int *ids, int T, int E, int S, int k, i
   // scatter the routed pairs
   for (int base = p0; base < p1; base += kWave) {
     const int q = base + lane;
-    const int e_q = q < p1 ? id_at(q) : 0;
+    const int e_q = q < p1 ? ids[q] : 0;
     const uint64_t m = match_lanes(e_q, q < p1);
     if (q < p1) o.rows[run_lds[w * kWave + e_q] + __popcll(m & below)] = (q / k) * nslot + (q % k);
     __builtin_amdgcn_wave_barrier();
