@@ -55,7 +55,7 @@ int max_tiles(const mv_config &c, int T, int tm) {
 int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T)); }
 
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, bcnt, total;
+  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -81,6 +81,7 @@ Layout layout(const mv_config &c, int T) {
   L.a = take(static_cast<size_t>(T) * nslot * c.d_ff * es);
   L.slots = take(static_cast<size_t>(T) * nslot * c.d_model * 4);
   L.argkey = take(static_cast<size_t>(T) * 8);
+  L.done = take(4);
   L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
   L.total = off;
   return L;
@@ -162,6 +163,7 @@ struct Step {
   float *slots() const { return reinterpret_cast<float *>(ws + L.slots); }
   float *gates() const { return reinterpret_cast<float *>(ws + L.gates); }
   unsigned long long *argkey() const { return reinterpret_cast<unsigned long long *>(ws + L.argkey); }
+  unsigned *done() const { return reinterpret_cast<unsigned *>(ws + L.done); }
 
   mv::RouteArgs route_args(int layer, int mode, int *ids, float *gates_out) const {
     mv::RouteArgs a{};
@@ -184,6 +186,7 @@ struct Step {
     if (mode == mv::kFinal) {
       a.gamma = w.final_norm;
       a.argkey = argkey();
+      a.done = done();
     } else if (mode == mv::kRoute) {
       const LayerPtrs lp = layer_ptrs(c, w, layer);
       a.gamma = lp.norm;
@@ -341,11 +344,10 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
     rc = st.route(L - 1, mv::kFinal, L == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, nullptr, nullptr);
   if (rc) return rc;
 
-  mv::LmArgs la{T, cfg->d_model, cfg->vocab, st.ws + st.L.x, w->lm_head, st.argkey()};
-  if ((rc = hip_status(mv::launch_lm_argmax(cfg->dtype, la, st.s)))) return rc;
-
-  mv::AcceptArgs aa{B, K, st.argkey(), nullptr, argmax, drafts, n_accepted, committed, n_committed};
-  return hip_status(mv::launch_accept(aa, st.s));
+  // LM head; its last block to finish applies the accept rule
+  const mv::AcceptArgs aa{B, K, st.argkey(), nullptr, argmax, drafts, n_accepted, committed, n_committed};
+  const mv::LmArgs la{T, cfg->d_model, cfg->vocab, st.ws + st.L.x, w->lm_head, st.argkey(), st.done(), aa};
+  return hip_status(mv::launch_lm_argmax(cfg->dtype, la, st.s));
 }
 
 MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_t *drafts,

@@ -24,14 +24,21 @@ namespace mv {
 
 namespace {
 
-constexpr int kGBM = 256;          // rows per tile
-constexpr int kGBN = 256;          // B rows per block
-constexpr int kGBK = 64;           // K per LDS stage
-constexpr int kGLd = kGBK + 16;    // LDS row stride in elements (160 bytes: conflict-free reads)
-constexpr int kGWavesM = 4;        // wavefront grid: 4 x 2 bands of 64 x 128
-constexpr int kGThreads = 64 * kGWavesM * 2;
-constexpr int kGWaveN = kGBN / 2;  // B rows per wavefront
-constexpr int kGroupTiles = 4;     // row tiles walked together per expert
+#ifndef MV_GEMM_BN
+#define MV_GEMM_BN 256
+#define MV_GEMM_BK 64
+#define MV_GEMM_PAD 16
+#endif
+constexpr int kGBM = 256;             // rows per tile
+constexpr int kGBN = MV_GEMM_BN;      // B rows per block
+constexpr int kGBK = MV_GEMM_BK;      // K per LDS stage
+constexpr int kGLd = kGBK + MV_GEMM_PAD;  // LDS row stride in elements (no bank conflicts)
+constexpr int kGWavesM = 4;           // wavefront grid: 4 x (kGBN / 128) bands of 64 x 128
+constexpr int kGWavesN = kGBN / 128;
+constexpr int kGThreads = 64 * kGWavesM * kGWavesN;
+constexpr int kGWaveN = kGBN / kGWavesN;  // B rows per wavefront
+constexpr int kGChunks = kGBK / 8;    // 16-byte chunks per row and K-step
+constexpr int kGroupTiles = 4;        // row tiles walked together per expert
 constexpr int kXcds = 8;
 
 struct GemmSmem {
@@ -63,26 +70,26 @@ __device__ bool gemm_item(const int *tile_start, int ne, int nb_count, int &tile
   return true;
 }
 
-// Global -> registers -> LDS copy of a [ROWS x kGBK] tile, 8 threads per row
-// (one 128-byte line per row and step); kStages steps are in flight in
-// registers, one slot per step.
+// Global -> registers -> LDS copy of a [ROWS x kGBK] tile, kGChunks threads
+// per row; kStages steps are in flight in registers, one slot per step.
 constexpr int kStages = 2;
 
 template <int ROWS>
 struct Stager {
-  static constexpr int PER = ROWS * (kGBK / 8) / kGThreads;
+  static constexpr int PER = ROWS * kGChunks / kGThreads;
   const bf16_t *src[PER];
   const bf16_t *alt[PER];  // source of K >= split (two operands laid end to end)
   int split = 1 << 30;
   uint4 reg[kStages][PER];
-  __device__ __forceinline__ static int row(int j) { return threadIdx.x / 8 + j * (kGThreads / 8); }
+  __device__ __forceinline__ static int row(int j) { return threadIdx.x / kGChunks + j * (kGThreads / kGChunks); }
+  __device__ __forceinline__ static int col() { return (threadIdx.x % kGChunks) * 8; }
   __device__ __forceinline__ void load(int slot, int k0) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) reg[slot][j] = ld16(k0 < split ? src[j] + k0 : alt[j] + (k0 - split));
   }
   __device__ __forceinline__ void store(int slot, bf16_t *lds) const {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) st16(lds + row(j) * kGLd + (threadIdx.x % 8) * 8, reg[slot][j]);
+    for (int j = 0; j < PER; ++j) st16(lds + row(j) * kGLd + col(), reg[slot][j]);
   }
 };
 
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_gate_up(ExpertArgs p) {
   const int4 tv = p.tile_info[tile];
   const int e = tv.x, r0 = tv.y, m = tv.z;
   const int n0 = nb * (kGBN / 2);
-  const int c8 = (threadIdx.x % 8) * 8;
+  const int c8 = Stager<kGBM>::col();
   Stager<kGBM> A;
   Stager<kGBN> B;
   const bf16_t *x = static_cast<const bf16_t *>(p.x);
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down(ExpertArgs p) {
   const int4 tv = p.tile_info[tile];
   const int e = tv.x, r0 = tv.y, m = tv.z;
   const int n0 = nb * kGBN;
-  const int c8 = (threadIdx.x % 8) * 8;
+  const int c8 = Stager<kGBM>::col();
   Stager<kGBM> A;
   Stager<kGBN> B;
   const bf16_t *a = static_cast<const bf16_t *>(p.a);
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down_shared(ExpertArgs p, Co
   const int in_group = min(kGroupTiles, nmt - g * kGroupTiles);
   const int nb = w / in_group, mt = g * kGroupTiles + (w - nb * in_group);
   const int t0 = mt * kGBM, n0 = nb * kGBN;
-  const int c8 = (threadIdx.x % 8) * 8;
+  const int c8 = Stager<kGBM>::col();
   const int S = p.S;
   const bf16_t *a = static_cast<const bf16_t *>(p.a);
   const bf16_t *W = static_cast<const bf16_t *>(p.w_shared);
@@ -372,27 +379,30 @@ hipError_t launch_gemm(KernelT kernel, int items, const ExpertArgs &a, hipStream
   return hipGetLastError();
 }
 
-// K = d: 20 steps for d = 1280; K = F: 14 steps for F = 896.
+// Unrolled K loops for the widths d = 1280 and F = 896.
+constexpr int kNkD = 1280 / kGBK, kNkF = 896 / kGBK;
+
 hipError_t launch_gemm_gate_up(const ExpertArgs &a, int max_tiles, hipStream_t s) {
   const int items = max_tiles * (a.F / (kGBN / 2));
-  return a.d == 20 * kGBK ? launch_gemm(k_gemm_gate_up<20>, items, a, s)
-                          : launch_gemm(k_gemm_gate_up<0>, items, a, s);
+  return a.d == kNkD * kGBK ? launch_gemm(k_gemm_gate_up<kNkD>, items, a, s)
+                            : launch_gemm(k_gemm_gate_up<0>, items, a, s);
 }
 
 hipError_t launch_gemm_down(const ExpertArgs &a, int max_tiles, hipStream_t s) {
   const int items = max_tiles * (a.d / kGBN);
-  return a.F == 14 * kGBK ? launch_gemm(k_gemm_down<14>, items, a, s)
-                          : launch_gemm(k_gemm_down<0>, items, a, s);
+  return a.F == kNkF * kGBK ? launch_gemm(k_gemm_down<kNkF>, items, a, s)
+                            : launch_gemm(k_gemm_down<0>, items, a, s);
 }
 
 hipError_t launch_gemm_down_shared(const ExpertArgs &a, const CombineArgs &c, hipStream_t s) {
   const int items = (a.T + kGBM - 1) / kGBM * (a.d / kGBN);
   const int grid = (items + kXcds - 1) / kXcds * kXcds;
-  const void *k = a.S == 2 && a.F == 14 * kGBK ? reinterpret_cast<const void *>(k_gemm_down_shared<28>)
-                                               : reinterpret_cast<const void *>(k_gemm_down_shared<0>);
+  const bool unrolled = a.S == 2 && a.F == kNkF * kGBK;
+  const void *k = unrolled ? reinterpret_cast<const void *>(k_gemm_down_shared<2 * kNkF>)
+                           : reinterpret_cast<const void *>(k_gemm_down_shared<0>);
   (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(GemmSmem));
-  if (a.S == 2 && a.F == 14 * kGBK)
-    hipLaunchKernelGGL(k_gemm_down_shared<28>, dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
+  if (unrolled)
+    hipLaunchKernelGGL(k_gemm_down_shared<2 * kNkF>, dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
   else
     hipLaunchKernelGGL(k_gemm_down_shared<0>, dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
   return hipGetLastError();

@@ -14,6 +14,53 @@ namespace mv {
 
 namespace {
 
+// Accept rule for sequence b: n = first j < K with drafts[j] != argmax[j]
+// (else K); committed = argmax[0..n], -1 after; n_committed = n + 1.  With
+// `coherent` the keys are read with agent-scope loads (keys folded by other
+// blocks of the same launch).
+__device__ void accept_sequence(const AcceptArgs &p, int b, bool coherent) {
+  const int K = p.K, base = b * (K + 1);
+  for (int j = 0; j <= K; ++j) {
+    int g;
+    if (p.argkey) {
+      const unsigned long long key =
+          coherent ? __hip_atomic_load(p.argkey + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : p.argkey[base + j];
+      g = static_cast<int>(key_index(key));
+    } else {
+      g = p.argmax_in[base + j];
+    }
+    if (p.argmax_out) p.argmax_out[base + j] = g;
+  }
+  const int *g = p.argkey ? p.argmax_out : p.argmax_in;
+  int n = 0;
+  while (n < K && p.drafts[b * K + n] == g[base + n]) ++n;
+  for (int j = 0; j <= K; ++j) p.committed[base + j] = j <= n ? g[base + j] : -1;
+  p.n_acc[b] = n;
+  p.n_com[b] = n + 1;
+}
+
+// After a block's atomicMax: wait for it to complete, count the block, and
+// in the last block to finish run the accept rule over every sequence.
+// The key updates are device-scope atomics and the last block reads the
+// keys with agent-scope loads, so no cache write-back is needed.
+__device__ void lm_block_done(const LmArgs &p) {
+  if (!p.done) return;
+  __shared__ int last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           gridDim.x * gridDim.y - 1;
+  __syncthreads();
+  if (!last) return;
+  for (int b = threadIdx.x; b < p.accept.B; b += blockDim.x) accept_sequence(p.accept, b, true);
+}
+
+}  // namespace
+
+namespace {
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -33,6 +80,7 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   }
   __syncthreads();
   lm_rows_block<T>(p, blockIdx.x, r0, m, A, lda, red, threadIdx.x);
+  lm_block_done(p);
 }
 
 // Up to 128 rows: every block takes all rows of its 16*MT-row group, so the
@@ -156,24 +204,13 @@ __global__ __launch_bounds__(64 * kLmMidWaves) void k_lm_argmax_mid(LmArgs p) {
     for (int w = 0; w < kLmMidWaves; ++w) k = red[w][row] > k ? red[w][row] : k;
     if (k != 0ull) atomicMax(p.argkey + rbase + row, static_cast<unsigned long long>(k));
   }
+  lm_block_done(p);
 }
 
-// One thread per sequence.  n = first j < K with drafts[j] != argmax[j]
-// (else K); committed = argmax[0..n], -1 after; n_committed = n + 1.
+// One thread per sequence.
 __global__ __launch_bounds__(256) void k_accept(AcceptArgs p) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= p.B) return;
-  const int K = p.K, base = b * (K + 1);
-  for (int j = 0; j <= K; ++j) {
-    const int g = p.argkey ? static_cast<int>(key_index(p.argkey[base + j])) : p.argmax_in[base + j];
-    if (p.argmax_out) p.argmax_out[base + j] = g;
-  }
-  const int *g = p.argkey ? p.argmax_out : p.argmax_in;
-  int n = 0;
-  while (n < K && p.drafts[b * K + n] == g[base + n]) ++n;
-  for (int j = 0; j <= K; ++j) p.committed[base + j] = j <= n ? g[base + j] : -1;
-  p.n_acc[b] = n;
-  p.n_com[b] = n + 1;
+  if (b < p.B) accept_sequence(p, b, false);
 }
 
 }  // namespace

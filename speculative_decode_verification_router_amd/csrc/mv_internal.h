@@ -46,6 +46,7 @@ struct RouteArgs {
   int *seg, *tile_start, *rows;
   int4 *tile_info;          // [max tiles] (expert, first row, rows, 0) per 16-row tile
   unsigned long long *argkey;  // kFinal: cleared
+  unsigned *done;           // kFinal: cleared (the LM head's block count)
 };
 
 // Combine of the previous layer's expert slots into the hidden state.
@@ -71,13 +72,6 @@ struct ExpertArgs {
   float *slots;            // [T*nslot, d]
 };
 
-struct LmArgs {
-  int T, d, V;
-  const void *xf;          // [T, d]
-  const void *w;           // [V, d]
-  unsigned long long *argkey;  // [T]
-};
-
 struct AcceptArgs {
   int B, K;
   const unsigned long long *argkey;  // [B*(K+1)] packed keys, or null
@@ -85,6 +79,15 @@ struct AcceptArgs {
   int *argmax_out;                   // may be null
   const int *drafts;                 // [B, K]
   int *n_acc, *committed, *n_com;
+};
+
+struct LmArgs {
+  int T, d, V;
+  const void *xf;          // [T, d]
+  const void *w;           // [V, d]
+  unsigned long long *argkey;  // [T]
+  unsigned *done;          // if set: blocks finished (zeroed beforehand); the last one runs `accept`
+  AcceptArgs accept;
 };
 
 // dtype-dispatched launchers (dtype: 0 fp32, 1 bf16); return the launch error.

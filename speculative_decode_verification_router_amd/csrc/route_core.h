@@ -197,6 +197,7 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   }
   if (a.mode == kFinal) {
     if (tid < nt) a.argkey[t0 + tid] = 0ull;
+    if (a.done && blockIdx.x == 0 && tid == 0) *a.done = 0u;
     return;
   }
   __syncthreads();
