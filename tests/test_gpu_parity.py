@@ -344,3 +344,37 @@ def test_lossless_gpu_decode_loop(bd, torch_cuda, tiny):
         step += 1
     assert seq[:n] == greedy[1:]
     assert step < n
+
+
+@pytest.mark.parametrize("B,K", [(1, 3), (8, 3)])
+def test_verify_step_in_a_graph(bd, torch_cuda, big, B, K):
+    """The verify step captured in a HIP graph: every replay, with eager
+    work on the stream between replays, equals the eager step bit for bit."""
+    torch = torch_cuda
+    dims, W, model = big
+    h = _dev(bd, synth.make_hidden(dims, B * (K + 1), seed=810 + B))
+    drafts = _dev(bd, np.random.default_rng(B).integers(0, dims.vocab, (B, K)).astype(np.int32))
+    ref = bd.run_verify_step(model, h, drafts, B, K)
+    _sync(torch)
+    ref = {k: _host(bd, v) for k, v in ref.items() if v is not None}
+    out = bd.run_verify_step(model, h, drafts, B, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bd.moe_verify_step(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
+                           out["n_accepted"], out["committed"], out["n_committed"], None, model.ws,
+                           model.ws_bytes, side)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bd.moe_verify_step(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
+                           out["n_accepted"], out["committed"], out["n_committed"], None, model.ws,
+                           model.ws_bytes, torch.cuda.current_stream())
+    for rep in range(3):
+        for v in out.values():
+            if v is not None:
+                v.fill_(-7)            # eager work between replays
+        graph.replay()
+        _sync(torch)
+        for key, want in ref.items():
+            assert np.array_equal(_host(bd, out[key]), want), (rep, key)
