@@ -1,10 +1,11 @@
 // Routing and grouping for large batches (bf16, the compute-bound path).
 //
-// k_route_large: 16 tokens per block.  RMSNorm with the canonical sum of
-// squares (route_core.h), then the router logits x W_r^T on the matrix cores
-// (v_mfma_f32_32x32x16_bf16; the products of bf16 values are exact and the
-// sums fp32, in the instruction's order, two K halves added), top-k by rank
-// as in route_core.h, and the block's per-expert pair counts.
+// k_route_large: 16 tokens per block of eight wavefronts.  Each wavefront
+// requests its router-weight fragments first, then RMSNorm with the canonical
+// sum of squares (route_core.h), the router logits x W_r^T on the matrix
+// cores (v_mfma_f32_32x32x16_bf16; the products of bf16 values are exact and
+// the sums fp32, in the instruction's order; four K quarters added in order),
+// top-k by rank as in route_core.h, and the block's per-expert pair counts.
 //
 // k_scatter: the stable grouping of the (token, slot) pairs by expert from
 // those counts.  Each block takes the same 16 tokens: the counts of the
@@ -21,7 +22,9 @@ namespace mv {
 namespace {
 
 constexpr int kRLTok = 16;       // tokens per routing block
-constexpr int kRLThreads = 256;  // 4 wavefronts
+constexpr int kRLThreads = 512;  // 8 wavefronts: 2 expert halves x 4 K quarters
+constexpr int kRLQuarterWin = 20;  // K windows per quarter held in registers (all of them for d <= 1280)
+constexpr int kScatterThreads = 256;
 
 struct RLSmem {
   size_t x, p, lg, inv, sel, total;
@@ -31,8 +34,8 @@ __host__ __device__ inline RLSmem rl_smem(int d) {
   RLSmem s;
   s.x = 0;                                                         // [17][d + 8] bf16: rows, then a zero row
   s.p = s.x + static_cast<size_t>(kRLTok + 1) * (d + 8) * 2;       // [16][nvec] fp32 chunk partials
-  s.lg = s.p + static_cast<size_t>(kRLTok) * nvec * 4;             // [2][32][64] fp32 logit halves
-  s.inv = s.lg + static_cast<size_t>(2) * 32 * 64 * 4;             // [16]
+  s.lg = s.p + static_cast<size_t>(kRLTok) * nvec * 4;             // [4][16][64] fp32 logit quarters
+  s.inv = s.lg + static_cast<size_t>(4) * kRLTok * 64 * 4;         // [16]
   s.sel = s.inv + kRLTok * 4;                                      // [16][8]
   s.total = s.sel + kRLTok * 8 * 4;
   return s;
@@ -52,6 +55,15 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   const int t0 = blockIdx.x * kRLTok, nt = min(kRLTok, a.T - t0);
 
   if (tid < 64) cnt[tid] = 0;
+  // router weights first: wavefront w takes experts 32*(w&1) .. +31 over K
+  // quarter w>>1, its fragments requested before the rows are read
+  const int nwin = d / 16, quarter = wv >> 1;
+  const int w_lo = quarter * nwin / 4, w_hi = (quarter + 1) * nwin / 4;
+  const int e_r = min(32 * (wv & 1) + (lane & 31), a.E - 1);
+  const bf16_t *wr = static_cast<const bf16_t *>(a.router_w) + static_cast<size_t>(e_r) * d + (lane >> 5) * 8;
+  uint4 b[kRLQuarterWin];
+#pragma unroll
+  for (int u = 0; u < kRLQuarterWin; ++u) b[u] = ld16(wr + min(w_lo + u, w_hi - 1) * 16);
   // rows, chunk partial sums of squares; rows nt..16 are zero (row 16 feeds
   // the MFMA tile's rows 16..31)
   for (int it0 = tid; it0 < (kRLTok + 1) * nvec; it0 += 4 * kRLThreads) {
@@ -102,36 +114,28 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   }
   __syncthreads();
 
-  // logits: wavefront w takes experts 32*(w&1) .. +31 over K half (w>>1)
-  {
-    const int nwin = d / 16, half = wv >> 1;
-    const int e = min(32 * (wv & 1) + (lane & 31), a.E - 1);
-    const bf16_t *wr = static_cast<const bf16_t *>(a.router_w) + static_cast<size_t>(e) * d + (lane >> 5) * 8;
+  {  // logits of this wavefront's experts over its K quarter; rows < 16 kept
     const bf16_t *xr = xl + min(lane & 31, kRLTok) * ld + (lane >> 5) * 8;
     f32x16_t acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    const int w_lo = half * nwin / 2, w_hi = (half + 1) * nwin / 2;
-    for (int w0 = w_lo; w0 < w_hi; w0 += 8) {
-      uint4 b[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) b[u] = ld16(wr + min(w0 + u, w_hi - 1) * 16);
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (w0 + u < w_hi) mfma32(acc, ld16(xr + (w0 + u) * 16), b[u]);
-    }
-    float *dst = lg + half * 32 * 64;
+    for (int u = 0; u < kRLQuarterWin; ++u)
+      if (w_lo + u < w_hi) mfma32(acc, ld16(xr + (w_lo + u) * 16), b[u]);
+    for (int w = w_lo + kRLQuarterWin; w < w_hi; ++w) mfma32(acc, ld16(xr + w * 16), ld16(wr + w * 16));
+    float *dst = lg + quarter * kRLTok * 64;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-      dst[row * 64 + 32 * (wv & 1) + (lane & 31)] = acc[q];
+      if (row < kRLTok) dst[row * 64 + 32 * (wv & 1) + (lane & 31)] = acc[q];
     }
   }
   __syncthreads();
   for (int i = tid; i < nt * 64; i += blockDim.x) {
     const int r = i / 64, e = i % 64;
-    const float b = (a.router_b && e < a.E) ? a.router_b[e] : 0.f;
-    lg[r * 64 + e] = (lg[r * 64 + e] + lg[32 * 64 + r * 64 + e]) + b;
+    const float bias = (a.router_b && e < a.E) ? a.router_b[e] : 0.f;
+    const float *q = lg + r * 64 + e;
+    lg[r * 64 + e] = (((q[0] + q[kRLTok * 64]) + q[2 * kRLTok * 64]) + q[3 * kRLTok * 64]) + bias;
   }
   __syncthreads();
   for (int r = wv; r < nt; r += kRLThreads / kWave)
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   if (tid < 64) blk_cnt[blockIdx.x * 64 + tid] = cnt[tid];
 }
 
-__global__ __launch_bounds__(kRLThreads) void k_scatter(RouteArgs a, const int *blk_cnt, int nblk) {
+__global__ __launch_bounds__(kScatterThreads) void k_scatter(RouteArgs a, const int *blk_cnt, int nblk) {
   __shared__ int part_tot[4][64], part_before[4][64];
   __shared__ int seg_e[64], base_e[64], first_run[64];
   __shared__ int ends[2];
@@ -248,7 +252,7 @@ hipError_t launch_route_large(const RouteArgs &a, const void *h, int *blk_cnt, h
                      blk_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(kRLThreads), 0, s, a, static_cast<const int *>(blk_cnt), nblk);
+  hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(kScatterThreads), 0, s, a, static_cast<const int *>(blk_cnt), nblk);
   return hipGetLastError();
 }
 
