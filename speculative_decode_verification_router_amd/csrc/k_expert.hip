@@ -2,84 +2,144 @@
 //
 // Up to 128 rows a block is one 16-row tile and one slice pair (the tile
 // parts of expert_core.h), with the tile's activation rows staged in LDS as
-// the MFMA A operand.  Small batches skip the separate grouping kernel: every gate/up block groups
-// the T*k routed pairs itself (one wavefront, a few ballots per expert) and
-// block (0, 0) also writes the grouping for the down kernel.
+// the MFMA A operand.  Small batches skip the separate grouping kernel: every
+// wavefront of a gate/up block finds its block's tile from the routing
+// itself, and the blocks of the first slice pair write the grouping for the
+// down kernel, each its own tile's entry.
 #include "expert_core.h"
 
 namespace mv {
 
 namespace {
 
-// Grouping of a small batch, built in LDS by every gate/up block.
-struct Grouping {
-  int cnt[kThreads], run[kThreads];
-  int seg[kMaxExperts + 1];
-  int tile_start[kMaxExperts + 1];
-  int rows[kSmallT * kMaxSlots];
-};
+// Tile `y` of the grouping table.  The entry is requested together with the
+// tile count, one round trip: the table holds an entry for every block of the
+// grid, and the test reads both, so neither load waits for the other.
+__device__ __forceinline__ bool table_tile(const ExpertArgs &p, int y, TileInfo &ti) {
+  const int4 v = p.tile_info[y];
+  const int n = p.tile_start[p.E + p.S];
+  if (y >= n || v.z <= 0) return false;
+  ti.e = v.x;
+  ti.r0 = v.y;
+  ti.m = v.z;
+  return true;
+}
 
-// Tile `tile` of the grouping: from the global table (large batches) or,
-// for small batches, by grouping the pairs in this block.
-__device__ bool block_tile(const ExpertArgs &p, int tile, TileInfo &ti, Grouping &g, bool write_global) {
-  const int ne = p.E + p.S;
-  if (!p.group_in_block) {
-    if (tile >= p.tile_start[ne]) return false;
-    const int4 v = p.tile_info[tile];
-    ti.e = v.x;
-    ti.r0 = v.y;
-    ti.m = v.z;
-    return true;
+// Small batches: every wavefront finds tile `y` of the grouping on its own,
+// with no block barrier, so the weights of the tile can be requested right
+// after the routing is read.  Per-expert pair counts by LDS atomics (lane e
+// reads expert e's count), an exclusive scan over the expert lanes gives the
+// segments and first tiles (shared expert s: segment T*k + s*T), a ballot
+// finds the expert whose tiles hold y, and the tile's rows are that expert's
+// pairs ranked by ballots in ascending pair order: the stable grouping.
+struct SmallTiles {
+  int cnt[kThreads / kWave][kWave];
+  int rows[kThreads / kWave][kTileM];  // pair id (t*nslot + slot) of each tile row
+};
+constexpr int kIdLoads = (kSmallT * kMaxTopK + kWave - 1) / kWave;  // id loads per lane
+
+__device__ bool small_tile(const ExpertArgs &p, int y, TileInfo &ti, SmallTiles &st, bool write_record) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int E = p.E, S = p.S, k = p.k, T = p.T, np = T * k, ne = E + S;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int v[kIdLoads];
+#pragma unroll
+  for (int i = 0; i < kIdLoads; ++i) v[i] = p.ids[min(i * kWave + lane, np - 1)];
+  int *cnt = st.cnt[w];
+  cnt[lane] = 0;
+#pragma unroll
+  for (int i = 0; i < kIdLoads; ++i) {
+    v[i] = min(max(v[i], 0), E - 1);  // ids are always in range; clamp defensively
+    if (i * kWave + lane < np) atomicAdd(&cnt[v[i]], 1);
   }
-  const GroupOut lds{g.seg, g.tile_start, g.rows, nullptr};
-  group_pairs(p.ids, p.T, p.E, p.S, p.k, p.nslot, kTileM, lds, g.cnt, g.run, kThreads / kWave);
-  __syncthreads();
-  if (write_global) {  // the grouping of record, for the down kernel
-    for (int i = threadIdx.x; i <= ne; i += blockDim.x) {
-      p.seg[i] = g.seg[i];
-      p.tile_start[i] = g.tile_start[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int c = lane < E ? cnt[lane] : 0;
+  const int tiles = (c + kTileM - 1) / kTileM;
+  int sc = c, stl = tiles;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int vc = __shfl_up(sc, off), vt = __shfl_up(stl, off);
+    if (lane >= off) { sc += vc; stl += vt; }
+  }
+  const int seg_e = sc - c, first_e = stl - tiles;
+  const int routed_tiles = __builtin_amdgcn_readlane(stl, kWave - 1);
+  const int shared_tiles = (T + kTileM - 1) / kTileM;
+  if (write_record) {  // segment and tile tables of record, for the down kernel
+    if (lane < E) {
+      p.seg[lane] = seg_e;
+      p.tile_start[lane] = first_e;
     }
-    for (int i = threadIdx.x; i < p.T * p.nslot; i += blockDim.x) p.rows[i] = g.rows[i];
-    for (int e = threadIdx.x; e < ne; e += blockDim.x) {
-      const int c = g.seg[e + 1] - g.seg[e];
-      for (int j = 0; j * kTileM < c; ++j)
-        p.tile_info[g.tile_start[e] + j] =
-            make_int4(e, g.seg[e] + j * kTileM, min(kTileM, c - j * kTileM), 0);
+    if (lane <= S) {
+      p.seg[E + lane] = np + lane * T;
+      p.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
     }
   }
-  if (tile >= g.tile_start[ne]) return false;
-  int e = 0;
-  while (e + 1 < ne && g.tile_start[e + 1] <= tile) ++e;
-  ti.e = e;
-  ti.r0 = g.seg[e] + (tile - g.tile_start[e]) * kTileM;
-  ti.m = min(kTileM, g.seg[e + 1] - ti.r0);
+  if (y >= routed_tiles + S * shared_tiles) return false;
+  int *rows = st.rows[w];
+  if (y < routed_tiles) {
+    const uint64_t hit = __ballot(lane < E && y >= first_e && y < first_e + tiles);
+    const int e = static_cast<int>(__builtin_ctzll(hit));
+    const int j = y - __builtin_amdgcn_readlane(first_e, e);
+    ti.e = e;
+    ti.r0 = __builtin_amdgcn_readlane(seg_e, e) + j * kTileM;
+    ti.m = min(kTileM, __builtin_amdgcn_readlane(c, e) - j * kTileM);
+    int run = 0;  // pairs of expert e before this batch of 64
+#pragma unroll
+    for (int i = 0; i < kIdLoads; ++i) {
+      const int q = i * kWave + lane;
+      const bool mine = q < np && v[i] == e;
+      const uint64_t m = __ballot(mine);
+      const int rr = run + __popcll(m & below) - j * kTileM;
+      if (mine && rr >= 0 && rr < kTileM) rows[rr] = (q / k) * p.nslot + (q % k);
+      run += __popcll(m);
+    }
+  } else {
+    const int s = (y - routed_tiles) / shared_tiles, j = y - routed_tiles - s * shared_tiles;
+    ti.e = E + s;
+    ti.r0 = np + s * T + j * kTileM;
+    ti.m = min(kTileM, T - j * kTileM);
+    if (lane < ti.m) rows[lane] = (j * kTileM + lane) * p.nslot + k + s;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   return true;
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ Grouping g;
+  __shared__ SmallTiles st;
   __shared__ float up_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
   TileInfo ti;
-  if (!block_tile(p, blockIdx.y, ti, g, p.group_in_block && blockIdx.x == 0 && blockIdx.y == 0))
+  const bool small = p.group_in_block != 0;
+  if (small ? !small_tile(p, blockIdx.y, ti, st, blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kWave)
+            : !table_tile(p, blockIdx.y, ti))
     return;
   GateUpPart<T> part;
   part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while x is staged
 
   const int d = p.d, nvec = d / VN, lda = d + VN;
-  const int *rows = p.group_in_block ? g.rows : p.rows;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (small && blockIdx.x == 0 && w == 0) {  // this tile's entry of the grouping of record
+    if (lane < ti.m) p.rows[ti.r0 + lane] = st.rows[0][lane];
+    if (lane == 0) p.tile_info[blockIdx.y] = make_int4(ti.e, ti.r0, ti.m, 0);
+  }
   T *A = reinterpret_cast<T *>(smem);
   const T *x = static_cast<const T *>(p.x);
   for (int it = threadIdx.x; it < kTileM * nvec; it += blockDim.x) {
     const int rr = it / nvec, c = it - rr * nvec;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < ti.m) v = ld16(x + static_cast<size_t>(rows[ti.r0 + rr] / p.nslot) * d + c * VN);
+    if (rr < ti.m) {
+      const int pair = small ? st.rows[w][rr] : p.rows[ti.r0 + rr];
+      v = ld16(x + static_cast<size_t>(pair / p.nslot) * d + c * VN);
+    }
     st16(A + rr * lda + c * VN, v);
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
   part.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, up_acc, threadIdx.x);
 }
 
@@ -88,9 +148,8 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float half_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
-  if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
-  const int4 tv = p.tile_info[blockIdx.y];
-  const TileInfo ti{tv.x, tv.y, tv.z};
+  TileInfo ti;
+  if (!table_tile(p, blockIdx.y, ti)) return;
   DownPart<T> part;
   part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while a is staged
   stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
@@ -146,9 +205,9 @@ __device__ __forceinline__ void mid_chain(f32x4_t (*acc)[MT], const T *const *ar
 template <typename T, int MT>
 __global__ __launch_bounds__(kThreads) void k_gate_up_mid(ExpertArgs p) {
   constexpr int VN = Vec<T>::N, WIN = 4 * VN;
-  if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
-  const int4 tv = p.tile_info[blockIdx.y];
-  const int e = tv.x, r0 = tv.y, m = tv.z;
+  TileInfo ti;
+  if (!table_tile(p, blockIdx.y, ti)) return;
+  const int e = ti.e, r0 = ti.r0, m = ti.m;
   const int d = p.d, F = p.F;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int f0 = (blockIdx.x * (kThreads / kWave) + wv) * 16;
@@ -188,9 +247,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_mid(ExpertArgs p) {
 template <typename T, int MT>
 __global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
   constexpr int VN = Vec<T>::N, WIN = 4 * VN;
-  if (blockIdx.y >= p.tile_start[p.E + p.S]) return;
-  const int4 tv = p.tile_info[blockIdx.y];
-  const int e = tv.x, r0 = tv.y, m = tv.z;
+  TileInfo ti;
+  if (!table_tile(p, blockIdx.y, ti)) return;
+  const int e = ti.e, r0 = ti.r0, m = ti.m;
   const int d = p.d, F = p.F;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * (kThreads / kWave) + wv) * 16;

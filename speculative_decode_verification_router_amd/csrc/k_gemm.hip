@@ -29,12 +29,17 @@ namespace {
 #define MV_GEMM_BK 64
 #define MV_GEMM_PAD 16
 #endif
+#ifndef MV_GEMM_WAVES_M
+#define MV_GEMM_WAVES_M 4
+#endif
 constexpr int kGBM = 256;             // rows per tile
 constexpr int kGBN = MV_GEMM_BN;      // B rows per block
 constexpr int kGBK = MV_GEMM_BK;      // K per LDS stage
 constexpr int kGLd = kGBK + MV_GEMM_PAD;  // LDS row stride in elements (no bank conflicts)
-constexpr int kGWavesM = 4;           // wavefront grid: 4 x (kGBN / 128) bands of 64 x 128
+constexpr int kGWavesM = MV_GEMM_WAVES_M;  // wavefront grid: kGWavesM x kGWavesN bands
 constexpr int kGWavesN = kGBN / 128;
+constexpr int kGWaveM = kGBM / kGWavesM;  // rows per wavefront
+constexpr int kGMT = kGWaveM / 32;        // 32-row MFMA tiles per wavefront
 constexpr int kGThreads = 64 * kGWavesM * kGWavesN;
 constexpr int kGWaveN = kGBN / kGWavesN;  // B rows per wavefront
 constexpr int kGChunks = kGBK / 8;    // 16-byte chunks per row and K-step
@@ -93,24 +98,24 @@ struct Stager {
   }
 };
 
-// Per wavefront: a 64 x kGWaveN output band as 2 x (kGWaveN / 32) tiles of 32x32.
-typedef f32x16_t GemmAcc[2][kGWaveN / 32];
+// Per wavefront: a kGWaveM x kGWaveN output band as kGMT x (kGWaveN / 32) tiles of 32x32.
+typedef f32x16_t GemmAcc[kGMT][kGWaveN / 32];
 
 // MFMAs of one K-step from LDS buffer `cur`.
 __device__ __forceinline__ void gemm_step(const GemmSmem &sm, int cur, GemmAcc &acc) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv % kGWavesM, wn = wv / kGWavesM;
-  const bf16_t *as = sm.a[cur] + (wm * 64 + (lane & 31)) * kGLd + (lane >> 5) * 8;
+  const bf16_t *as = sm.a[cur] + (wm * kGWaveM + (lane & 31)) * kGLd + (lane >> 5) * 8;
   const bf16_t *bs = sm.b[cur] + (wn * kGWaveN + (lane & 31)) * kGLd + (lane >> 5) * 8;
 #pragma unroll
   for (int u = 0; u < kGBK / 16; ++u) {
-    uint4 af[2], bfr[kGWaveN / 32];
+    uint4 af[kGMT], bfr[kGWaveN / 32];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) af[i] = ld16(as + i * 32 * kGLd + u * 16);
+    for (int i = 0; i < kGMT; ++i) af[i] = ld16(as + i * 32 * kGLd + u * 16);
 #pragma unroll
     for (int j = 0; j < kGWaveN / 32; ++j) bfr[j] = ld16(bs + j * 32 * kGLd + u * 16);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kGMT; ++i)
 #pragma unroll
       for (int j = 0; j < kGWaveN / 32; ++j) mfma32(acc[i][j], af[i], bfr[j]);
   }
@@ -120,7 +125,7 @@ __device__ __forceinline__ void gemm_step(const GemmSmem &sm, int cur, GemmAcc &
 // B row of its column in tile j.
 __device__ __forceinline__ int gemm_row(int i, int q) {
   const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) % kGWavesM;
-  return wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+  return wm * kGWaveM + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
 }
 __device__ __forceinline__ int gemm_col(int j) {
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) / kGWavesM;
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_gate_up(ExpertArgs p) {
   }
   GemmAcc acc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGMT; ++i)
 #pragma unroll
     for (int j = 0; j < kGWaveN / 32; ++j)
 #pragma unroll
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_gate_up(ExpertArgs p) {
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) / kGWavesM;
   bf16_t *aout = static_cast<bf16_t *>(p.a_out);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGMT; ++i)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = gemm_row(i, q);
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down(ExpertArgs p) {
     B.src[j] = W + static_cast<size_t>(n0 + Stager<kGBN>::row(j)) * F + c8;
   GemmAcc acc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGMT; ++i)
 #pragma unroll
     for (int j = 0; j < kGWaveN / 32; ++j)
 #pragma unroll
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down(ExpertArgs p) {
   gemm_mainloop<NK>(sm, A, B, F / kGBK, acc);
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGMT; ++i)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = gemm_row(i, q);
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down_shared(ExpertArgs p, Co
   }
   GemmAcc acc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGMT; ++i)
 #pragma unroll
     for (int j = 0; j < kGWaveN / 32; ++j)
 #pragma unroll
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down_shared(ExpertArgs p, Co
   bf16_t *hd = static_cast<bf16_t *>(c.h_dst);
   constexpr int NJ = kGWaveN / 32;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGMT; ++i)
 #pragma unroll 4
     for (int qq = 0; qq < 16; ++qq) {
       const int t_raw = t0 + gemm_row(i, qq), t = min(t_raw, T - 1);

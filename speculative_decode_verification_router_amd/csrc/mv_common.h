@@ -65,6 +65,40 @@ __device__ __forceinline__ uint4 pack(const float *v, bf16_t) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Half of a 16-byte vector (8 bytes): 4 bf16 or 2 fp32 elements.
+__device__ __forceinline__ void unpack8(const uint2 &q, float *out, float) {
+  out[0] = __uint_as_float(q.x); out[1] = __uint_as_float(q.y);
+}
+__device__ __forceinline__ void unpack8(const uint2 &q, float *out, bf16_t) {
+  out[0] = __uint_as_float(q.x << 16); out[1] = __uint_as_float(q.x & 0xffff0000u);
+  out[2] = __uint_as_float(q.y << 16); out[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+__device__ __forceinline__ uint2 pack8(const float *v, float) {
+  return make_uint2(__float_as_uint(v[0]), __float_as_uint(v[1]));
+}
+__device__ __forceinline__ uint2 pack8(const float *v, bf16_t) {
+  return make_uint2(static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                    static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+}
+__device__ __forceinline__ uint2 ld8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
+__device__ __forceinline__ void st8(void *p, const uint2 &v) { *reinterpret_cast<uint2 *>(p) = v; }
+
+// N consecutive fp32 values (N = 2 or 4) as one vector load or store.
+template <int N> __device__ __forceinline__ void ld_f32(const float *p, float *o) {
+  if constexpr (N == 4) {
+    const float4 q = *reinterpret_cast<const float4 *>(p);
+    o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
+  } else {
+    static_assert(N == 2, "2 or 4 values");
+    const float2 q = *reinterpret_cast<const float2 *>(p);
+    o[0] = q.x; o[1] = q.y;
+  }
+}
+template <int N> __device__ __forceinline__ void st_f32(float *p, const float *v) {
+  if constexpr (N == 4) *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  else *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+}
+
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {

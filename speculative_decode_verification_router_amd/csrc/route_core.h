@@ -100,13 +100,14 @@ __device__ __forceinline__ void select_top_k(const float *lg_row, float *sel_lds
 
 // LDS layout of a routing block holding `ntok` token rows.
 struct RouteSmem {
-  size_t h, p, lg, inv, sel, total;
+  size_t h, g, p, lg, inv, sel, total;
 };
 __host__ __device__ inline RouteSmem route_smem(int ntok, int d, int elem_bytes) {
   const int vn = 16 / elem_bytes, nvec = d / vn;
   RouteSmem s;
   s.h = 0;                                                        // [ntok][d + vn] storage T
-  s.p = s.h + static_cast<size_t>(ntok) * (d + vn) * elem_bytes;  // [ntok][nvec] fp32 partials
+  s.g = s.h + static_cast<size_t>(ntok) * (d + vn) * elem_bytes;  // [d] gamma, storage T
+  s.p = s.g + static_cast<size_t>(d) * elem_bytes;                // [ntok][nvec] fp32 partials
   s.lg = s.p + static_cast<size_t>(ntok) * nvec * 4;              // [ntok][64] logits
   s.inv = s.lg + static_cast<size_t>(ntok) * 64 * 4;              // [ntok]
   s.sel = s.inv + static_cast<size_t>(ntok) * 4;                  // [ntok][8]
@@ -128,46 +129,75 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   float *sel = reinterpret_cast<float *>(smem + L.sel);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // router weights first: their latency overlaps the combine and the norm
+  // Every load of the first phase is requested before any is used, so the
+  // block waits on one memory round trip: the router weights, gamma, the rows
+  // and all of their slots.
   uint4 wq[kRouterChunks];
   if (a.mode == kRoute) router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, 4 * wv, d);
+  T *gl = reinterpret_cast<T *>(smem + L.g);
+  uint4 gv = make_uint4(0, 0, 0, 0);
+  if (a.mode != kCombine && tid < nvec) gv = ld16(static_cast<const T *>(a.gamma) + tid * VN);
 
-  // combine (or plain load) of the rows, chunk partial sums of squares
+  // combine (or plain load) of the rows: two adjacent lanes per chunk, HV
+  // elements each.  The lower lane's running sum of squares is handed to the
+  // upper one, which continues it, so each chunk partial keeps the sequential
+  // order over the chunk's VN elements.
+  constexpr int HV = VN / 2;
+  constexpr int kSlotBatch = 8;  // slot loads in flight per lane
   const T *hs = static_cast<const T *>(c.h_src);
-  for (int it = tid; it < nt * nvec; it += blockDim.x) {
-    const int r = it / nvec, ch = it % nvec, t = t0 + r;
-    float h[VN];
-    unpack(ld16(hs + static_cast<size_t>(t) * d + ch * VN), h, T());
+  for (int it = tid; it < nt * nvec * 2; it += blockDim.x) {
+    const int r = it / (2 * nvec), hc = it - r * 2 * nvec, ch = hc >> 1, half = hc & 1;
+    const int t = t0 + r;
+    const int col = ch * VN + half * HV;
+    const T *hrow = hs + static_cast<size_t>(t) * d + col;
+    float h[HV];
     if (c.slots) {
-      float y[VN];
+      // slot loads first, index clamped so every load is unconditional; a
+      // surplus slot adds -0, which leaves every sum unchanged
+      const float *sp = c.slots + static_cast<size_t>(t) * a.nslot * d + col;
+      float v[kSlotBatch][HV], y[HV];
 #pragma unroll
-      for (int i = 0; i < VN; ++i) y[i] = 0.f;
-      const float *sp = c.slots + static_cast<size_t>(t) * a.nslot * d + ch * VN;
-      for (int s = 0; s < a.nslot; ++s) {
+      for (int s = 0; s < kSlotBatch; ++s)
+        ld_f32<HV>(sp + static_cast<size_t>(min(s, a.nslot - 1)) * d, v[s]);
+      const uint2 hq = ld8(hrow);
 #pragma unroll
-        for (int i = 0; i < VN; i += 4) {
-          const float4 v = *reinterpret_cast<const float4 *>(sp + static_cast<size_t>(s) * d + i);
-          y[i] += v.x; y[i + 1] += v.y; y[i + 2] += v.z; y[i + 3] += v.w;
-        }
+      for (int i = 0; i < HV; ++i) y[i] = 0.f + v[0][i];  // nslot >= 1 whenever slots are combined
+#pragma unroll
+      for (int s = 1; s < kSlotBatch; ++s)
+#pragma unroll
+        for (int i = 0; i < HV; ++i) y[i] += s < a.nslot ? v[s][i] : -0.f;
+      for (int s0 = kSlotBatch; s0 < a.nslot; s0 += kSlotBatch) {
+#pragma unroll
+        for (int s = 0; s < kSlotBatch; ++s)
+          ld_f32<HV>(sp + static_cast<size_t>(min(s0 + s, a.nslot - 1)) * d, v[s]);
+#pragma unroll
+        for (int s = 0; s < kSlotBatch; ++s)
+#pragma unroll
+          for (int i = 0; i < HV; ++i) y[i] += s0 + s < a.nslot ? v[s][i] : -0.f;
       }
+      unpack8(hq, h, T());
 #pragma unroll
-      for (int i = 0; i < VN; ++i) h[i] = round_to<T>(h[i] + y[i]);
-      if (c.y_moe) {
-        float *yp = c.y_moe + static_cast<size_t>(t) * d + ch * VN;
-#pragma unroll
-        for (int i = 0; i < VN; i += 4)
-          *reinterpret_cast<float4 *>(yp + i) = make_float4(y[i], y[i + 1], y[i + 2], y[i + 3]);
-      }
+      for (int i = 0; i < HV; ++i) h[i] = round_to<T>(h[i] + y[i]);
+      if (c.y_moe) st_f32<HV>(c.y_moe + static_cast<size_t>(t) * d + col, y);
+    } else {
+      unpack8(ld8(hrow), h, T());
     }
     float p = 0.f;
 #pragma unroll
-    for (int i = 0; i < VN; ++i) p += h[i] * h[i];
-    const uint4 pk = pack(h, T());
-    st16(hl + r * ld + ch * VN, pk);
-    if (c.slots && c.h_dst) st16(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + ch * VN, pk);
-    pl[r * nvec + ch] = p;
+    for (int i = 0; i < HV; ++i) p += h[i] * h[i];
+    const float lower = __shfl_xor(p, 1);
+    if (half) {
+      p = lower;
+#pragma unroll
+      for (int i = 0; i < HV; ++i) p += h[i] * h[i];
+      pl[r * nvec + ch] = p;
+    }
+    const uint2 pk = pack8(h, T());
+    st8(hl + r * ld + col, pk);
+    if (c.slots && c.h_dst) st8(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + col, pk);
   }
   if (a.mode == kCombine) return;
+  if (tid < nvec) st16(gl + tid * VN, gv);
   __syncthreads();
 
   // per-token sum of squares (wavefront r handles token r) and 1/rms
@@ -181,13 +211,12 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   __syncthreads();
 
   // x = round(h * inv * gamma): to LDS (router operand) and to x_out
-  const T *gam = static_cast<const T *>(a.gamma);
   T *xo = static_cast<T *>(a.x_out);
   for (int it = tid; it < nt * nvec; it += blockDim.x) {
     const int r = it / nvec, ch = it % nvec;
     float hv[VN], g[VN], x[VN];
     unpack(ld16(hl + r * ld + ch * VN), hv, T());
-    unpack(ld16(gam + ch * VN), g, T());
+    unpack(ld16(gl + ch * VN), g, T());
     const float s = inv[r];
 #pragma unroll
     for (int i = 0; i < VN; ++i) x[i] = round_to<T>((hv[i] * s) * g[i]);
