@@ -27,7 +27,7 @@ constexpr int kRLQuarterWin = 20;  // K windows per quarter held in registers (a
 constexpr int kScatterThreads = 256;
 
 struct RLSmem {
-  size_t x, p, lg, inv, sel, total;
+  size_t x, p, lg, key, inv, sel, total;
 };
 __host__ __device__ inline RLSmem rl_smem(int d) {
   const int nvec = d / 8;
@@ -35,9 +35,10 @@ __host__ __device__ inline RLSmem rl_smem(int d) {
   s.x = 0;                                                         // [17][d + 8] bf16: rows, then a zero row
   s.p = s.x + static_cast<size_t>(kRLTok + 1) * (d + 8) * 2;       // [16][nvec] fp32 chunk partials
   s.lg = s.p + static_cast<size_t>(kRLTok) * nvec * 4;             // [4][16][64] fp32 logit quarters
-  s.inv = s.lg + static_cast<size_t>(4) * kRLTok * 64 * 4;         // [16]
-  s.sel = s.inv + kRLTok * 4;                                      // [16][8]
-  s.total = s.sel + kRLTok * 8 * 4;
+  s.key = s.lg + static_cast<size_t>(4) * kRLTok * 64 * 4;         // [16][64] top-k keys
+  s.inv = s.key + static_cast<size_t>(kRLTok) * 64 * 8;            // [16]
+  s.sel = s.inv + kRLTok * 4;                                      // [16][kMaxTopK]
+  s.total = s.sel + kRLTok * kMaxTopK * 4;
   return s;
 }
 
@@ -51,6 +52,7 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   float *lg = reinterpret_cast<float *>(smem + L.lg);
   float *inv = reinterpret_cast<float *>(smem + L.inv);
   float *sel = reinterpret_cast<float *>(smem + L.sel);
+  uint64_t *keys = reinterpret_cast<uint64_t *>(smem + L.key);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int t0 = blockIdx.x * kRLTok, nt = min(kRLTok, a.T - t0);
 
@@ -139,7 +141,8 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   }
   __syncthreads();
   for (int r = wv; r < nt; r += kRLThreads / kWave)
-    select_top_k(lg + r * 64, sel + r * 8, a.E, a.k, a.ids + (t0 + r) * a.k, a.gates + (t0 + r) * a.k);
+    select_top_k(lg + r * 64, keys + r * 64, sel + r * kMaxTopK, a.E, a.k, a.ids + (t0 + r) * a.k,
+                 a.gates + (t0 + r) * a.k);
   __syncthreads();
   for (int i = tid; i < nt * a.k; i += blockDim.x) atomicAdd(&cnt[a.ids[t0 * a.k + i]], 1);
   __syncthreads();

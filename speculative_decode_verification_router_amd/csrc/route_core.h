@@ -73,15 +73,27 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
 }
 
 // Top-k of one token's logits lg_row[0..E) on one wavefront: lane e's rank
-// is the number of experts ordered before it by (logit desc, id asc).
-__device__ __forceinline__ void select_top_k(const float *lg_row, float *sel_lds, int E, int k,
-                                             int *ids, float *gates) {
+// is the number of experts ordered before it by (logit desc, id asc).  Each
+// lane's (logit, id) key goes to LDS once (lanes >= E write 0, below every
+// real key) and every lane counts the keys above its own, two per read.
+// key_lds: 64 keys, 16-byte aligned; sel_lds: kMaxTopK floats.
+__device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_lds, float *sel_lds, int E,
+                                             int k, int *ids, float *gates) {
   const int lane = threadIdx.x & 63;
   const float logit = lg_row[lane];
-  const uint64_t mine = argmax_key(logit, static_cast<uint32_t>(lane));
+  const uint64_t mine = lane < E ? argmax_key(logit, static_cast<uint32_t>(lane)) : 0ull;
+  key_lds[lane] = mine;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint4 *kv = reinterpret_cast<const uint4 *>(key_lds);
   int rank = 0;
-#pragma unroll 16
-  for (int j = 0; j < E; ++j) rank += argmax_key(lg_row[j], static_cast<uint32_t>(j)) > mine;
+#pragma unroll
+  for (int j = 0; j < kWave / 2; ++j) {
+    const uint4 two = kv[j];
+    rank += ((static_cast<uint64_t>(two.y) << 32 | two.x) > mine) +
+            ((static_cast<uint64_t>(two.w) << 32 | two.z) > mine);
+  }
   const bool chosen = lane < E && rank < k;
   const uint64_t top = __ballot(chosen && rank == 0);
   const float vmax = __shfl(logit, static_cast<int>(__builtin_ctzll(top)));
@@ -93,14 +105,19 @@ __device__ __forceinline__ void select_top_k(const float *lg_row, float *sel_lds
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float den = 0.f;
-  for (int s = 0; s < k; ++s) den += sel_lds[s];
+  // denominator in rank order; every entry is read, a surplus one adds -0
+  float v[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) v[s] = sel_lds[s];
+  float den = 0.f + v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxTopK; ++s) den += s < k ? v[s] : -0.f;
   if (chosen) gates[rank] = ex / den;
 }
 
 // LDS layout of a routing block holding `ntok` token rows.
 struct RouteSmem {
-  size_t h, g, p, lg, inv, sel, total;
+  size_t h, g, p, lg, key, inv, sel, total;
 };
 __host__ __device__ inline RouteSmem route_smem(int ntok, int d, int elem_bytes) {
   const int vn = 16 / elem_bytes, nvec = d / vn;
@@ -109,9 +126,10 @@ __host__ __device__ inline RouteSmem route_smem(int ntok, int d, int elem_bytes)
   s.g = s.h + static_cast<size_t>(ntok) * (d + vn) * elem_bytes;  // [d] gamma, storage T
   s.p = s.g + static_cast<size_t>(d) * elem_bytes;                // [ntok][nvec] fp32 partials
   s.lg = s.p + static_cast<size_t>(ntok) * nvec * 4;              // [ntok][64] logits
-  s.inv = s.lg + static_cast<size_t>(ntok) * 64 * 4;              // [ntok]
-  s.sel = s.inv + static_cast<size_t>(ntok) * 4;                  // [ntok][8]
-  s.total = s.sel + static_cast<size_t>(ntok) * 8 * 4;
+  s.key = s.lg + static_cast<size_t>(ntok) * 64 * 4;              // [ntok][64] top-k keys
+  s.inv = s.key + static_cast<size_t>(ntok) * 64 * 8;             // [ntok]
+  s.sel = s.inv + static_cast<size_t>(ntok) * 4;                  // [ntok][kMaxTopK]
+  s.total = s.sel + static_cast<size_t>(ntok) * kMaxTopK * 4;
   return s;
 }
 
@@ -127,6 +145,7 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   float *lg = reinterpret_cast<float *>(smem + L.lg);
   float *inv = reinterpret_cast<float *>(smem + L.inv);
   float *sel = reinterpret_cast<float *>(smem + L.sel);
+  uint64_t *keys = reinterpret_cast<uint64_t *>(smem + L.key);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   // Every load of the first phase is requested before any is used, so the
@@ -235,7 +254,8 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
     router_rows<T>(wq, hl, ld, nt, d, static_cast<const T *>(a.router_w), a.router_b, a.E, 4 * wv, lg);
   __syncthreads();
   for (int r = wv; r < nt; r += blockDim.x / kWave)
-    select_top_k(lg + r * 64, sel + r * 8, a.E, a.k, a.ids + (t0 + r) * a.k, a.gates + (t0 + r) * a.k);
+    select_top_k(lg + r * 64, keys + r * 64, sel + r * kMaxTopK, a.E, a.k, a.ids + (t0 + r) * a.k,
+                 a.gates + (t0 + r) * a.k);
 }
 
 // ---------------------------------------------------------------- grouping
