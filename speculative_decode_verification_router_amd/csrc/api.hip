@@ -55,7 +55,7 @@ int max_tiles(const mv_config &c, int T, int tm) {
 int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T)); }
 
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, total;
+  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, logits, tdone, total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -83,6 +83,8 @@ Layout layout(const mv_config &c, int T) {
   L.argkey = take(static_cast<size_t>(T) * 8);
   L.done = take(4);
   L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
+  L.logits = take(static_cast<size_t>(T) * 64 * 4);
+  L.tdone = take((static_cast<size_t>(max_tiles(c, T, mv::kTileM)) + 1) * mv::kDoneStride * 4);  // + the timeout word
   L.total = off;
   return L;
 }
@@ -197,14 +199,26 @@ struct Step {
   }
 
   bool small() const { return T <= mv::kSmallT; }
+  // Router logits spread over expert groups, top-k in the gate/up kernel.
+  bool logits_route() const { return T <= mv::kLogitsMaxT; }
+  float *logits() const { return reinterpret_cast<float *>(ws + L.logits); }
+  unsigned *tile_done() const { return reinterpret_cast<unsigned *>(ws + L.tdone); }
   // LDS-tiled GEMMs; the combine is in the shared experts' down projection
   bool gemm() const { return path_for(c, T) == kGemmTiles; }
 
   // One routing launch (+ the grouping kernel on the large-batch path).
   // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
+  // `logits`: routing stops at the logits (mode kRoute only; the ffn of the
+  // same layer then takes the top-k).
   int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
-            float *y_moe, int *ids, float *gates_out) const {
+            float *y_moe, int *ids, float *gates_out, bool logits = false) const {
     mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
+    if (logits && mode == mv::kRoute) {
+      a.mode = mv::kLogits;
+      a.logits = this->logits();
+      a.tile_done = tile_done();
+      a.n_tile_done = max_tiles(c, T, mv::kTileM);
+    }
     if (mode == mv::kRoute && gemm()) {  // h_src is already combined on this path
       return hip_status(mv::launch_route_large(a, h_src, reinterpret_cast<int *>(ws + L.bcnt), s));
     }
@@ -221,8 +235,10 @@ struct Step {
 
   // gate/up then down for `layer`, leaving the weighted expert outputs in
   // slots; on the GEMM path also the combine h_dst = h_src + y (y_moe: y).
-  int ffn(int layer, const int *ids_in, const float *gates_in, const void *h_src = nullptr,
-          void *h_dst = nullptr, float *y_moe = nullptr) const {
+  // `logits`: the routing of this layer stopped at the logits; the gate/up
+  // kernel takes the top-k and writes ids and gates.
+  int ffn(int layer, int *ids, float *gates, const void *h_src = nullptr, void *h_dst = nullptr,
+          float *y_moe = nullptr, bool logits = false) const {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e{};
     e.T = T;
@@ -239,13 +255,23 @@ struct Step {
     e.tile_start = tiles();
     e.rows = rows();
     e.tile_info = tinfo();
-    e.ids = ids_in;
+    e.ids = ids;
     e.group_in_block = small() ? 1 : 0;
-    e.gates = gates_in;
+    e.gates = gates;
     e.slots = slots();
     const int mt = max_tiles(c, T);
     e.w_routed = lp.gu;
     e.w_shared = lp.sgu;
+    if (logits) {  // gate/up and down in one launch
+      e.logits = this->logits();
+      e.ids_out = ids;
+      e.gates_out = gates;
+      e.tile_done = tile_done();
+      e.err = tile_done() + static_cast<size_t>(max_tiles(c, T, mv::kTileM)) * mv::kDoneStride;
+      e.w_routed_down = lp.down;
+      e.w_shared_down = lp.sdown;
+      return hip_status(mv::launch_ffn_small(c.dtype, e, mt, s));
+    }
     const Path path = path_for(c, T);
     int rc = hip_status(path == kGemmTiles  ? mv::launch_gemm_gate_up(e, mt, s)
                         : path == kMidTiles ? mv::launch_gate_up_mid(c.dtype, e, mt, s)
@@ -332,11 +358,12 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
       continue;
     }
     // layer 0 routes h_in; later layers first add the previous layer's experts
+    const bool lg = st.logits_route();
     if (layer == 0)
-      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates);
+      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, lg);
     else
-      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates);
-    if (rc || (rc = st.ffn(layer, ids, gates))) return rc;
+      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates, lg);
+    if (rc || (rc = st.ffn(layer, ids, gates, nullptr, nullptr, nullptr, lg))) return rc;
   }
   if (gemm)
     rc = st.route(L - 1, mv::kFinal, hbuf, nullptr, nullptr, nullptr, nullptr, nullptr);

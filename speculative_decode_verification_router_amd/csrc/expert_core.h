@@ -27,9 +27,14 @@ struct TileInfo {
 };
 
 template <typename T>
+__device__ __forceinline__ const T *expert_base(const void *w_routed, const void *w_shared, int E, int e,
+                                               size_t elems) {
+  return e < E ? static_cast<const T *>(w_routed) + static_cast<size_t>(e) * elems
+               : static_cast<const T *>(w_shared) + static_cast<size_t>(e - E) * elems;
+}
+template <typename T>
 __device__ __forceinline__ const T *expert_base(const ExpertArgs &p, int e, size_t elems) {
-  return e < p.E ? static_cast<const T *>(p.w_routed) + static_cast<size_t>(e) * elems
-                 : static_cast<const T *>(p.w_shared) + static_cast<size_t>(e - p.E) * elems;
+  return expert_base<T>(p.w_routed, p.w_shared, p.E, e, elems);
 }
 
 // Weight loads of windows [w0, min(w0 + kUnroll, w_hi)) into registers.
@@ -58,7 +63,10 @@ __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b,
 }
 
 // The tile's a rows (zero-filled past m) into LDS, row stride F + one vector.
-template <typename T>
+// kCoherent: a was written by other blocks of the same launch (write-through
+// stores), so it is read with agent-scope loads, which no stale cache line
+// can answer.
+template <typename T, bool kCoherent = false>
 __device__ __forceinline__ void stage_a_tile(const ExpertArgs &p, const TileInfo &ti, T *A, int tid, int nthreads) {
   constexpr int VN = Vec<T>::N;
   const int F = p.F, nvec = F / VN, lda = F + VN;
@@ -66,9 +74,33 @@ __device__ __forceinline__ void stage_a_tile(const ExpertArgs &p, const TileInfo
   for (int it = tid; it < kTileM * nvec; it += nthreads) {
     const int rr = it / nvec, c = it - rr * nvec;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < ti.m) v = ld16(a + static_cast<size_t>(ti.r0 + rr) * F + c * VN);
+    if (rr < ti.m) {
+      const T *src = a + static_cast<size_t>(ti.r0 + rr) * F + c * VN;
+      if constexpr (kCoherent) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(src);
+        v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        v = ld16(src);
+      }
+    }
     st16(A + rr * lda + c * VN, v);
   }
+}
+
+// Write-through store of one value per lane, the lanes of a pair holding
+// adjacent columns (bf16: the even lane stores both as one 32-bit word; both
+// lanes of the pair must call this).
+__device__ __forceinline__ void store_through(float *p, float v, int) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_through(bf16_t *p, float v, int lane) {
+  const uint32_t mine = f32_to_bf16(v), other = __shfl_xor(mine, 1);
+  if (!(lane & 1))
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), mine | (other << 16), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // gate/up of slice pair `pair` of a tile.  begin() issues the first weight
@@ -91,6 +123,9 @@ struct GateUpPart {
     b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
     load_batch<T>(q, b, 0, nwin);
   }
+  // kThrough: a is written with write-through stores (read by other blocks
+  // of the same launch).
+  template <bool kThrough = false>
   __device__ __forceinline__ void finish(const ExpertArgs &p, const TileInfo &ti, const T *arow,
                                          float (*up_acc)[64][4], int tid) {
     const int lane = tid & 63, F = p.F;
@@ -108,19 +143,24 @@ struct GateUpPart {
       const int row = (lane >> 4) * 4 + i;
       if (row < ti.m) {
         const float gv = acc[i], uv = up_acc[slice][lane][i];
-        aout[static_cast<size_t>(ti.r0 + row) * F + f0 + (lane & 15)] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
+        const float v = gv / (1.0f + expf(-gv)) * uv;
+        T *dst = aout + static_cast<size_t>(ti.r0 + row) * F + f0 + (lane & 15);
+        if constexpr (kThrough) store_through(dst, v, lane);
+        else *dst = from_f32<T>(v);
       }
     }
   }
 };
 
-// down of slice pair `pair` of a tile; same split as GateUpPart.
+// down of slice pair `pair` of a tile; same split as GateUpPart.  The down
+// weights are p.w_routed / p.w_shared unless given.
 template <typename T>
 struct DownPart {
   const T *b;
   int n0, half, slice, w_lo, w_hi;
   uint4 q[kUnroll];
-  __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid) {
+  __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid,
+                                        const void *w_routed = nullptr, const void *w_shared = nullptr) {
     constexpr int VN = Vec<T>::N;
     const int lane = tid & 63, wv = tid >> 6;
     slice = wv >> 1;
@@ -130,12 +170,16 @@ struct DownPart {
     const int nwin = F / (4 * VN);
     w_lo = n0 < d ? half * nwin / 2 : 0;
     w_hi = n0 < d ? (half + 1) * nwin / 2 : 0;
-    const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
+    const T *W = w_routed ? expert_base<T>(w_routed, w_shared, p.E, ti.e, static_cast<size_t>(d) * F)
+                          : expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
     b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
     load_batch<T>(q, b, w_lo, w_hi);
   }
+  // tile_rows[row]: the pair id (t*nslot + slot) of tile row `row`; gates:
+  // [T, k] softmax gates of the routed pairs.
   __device__ __forceinline__ void finish(const ExpertArgs &p, const TileInfo &ti, const T *arow,
-                                         float (*half_acc)[64][4], int tid) {
+                                         float (*half_acc)[64][4], int tid, const int *tile_rows,
+                                         const float *gates) {
     const int lane = tid & 63, d = p.d;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     mfma_panel<T>(acc, arow, b, w_lo, w_hi, q);
@@ -149,9 +193,9 @@ struct DownPart {
     for (int i = 0; i < 4; ++i) {
       const int row = (lane >> 4) * 4 + i;
       if (row < ti.m) {
-        const int pair = p.rows[ti.r0 + row];
+        const int pair = tile_rows[row];
         const int tok = pair / p.nslot, s = pair - tok * p.nslot;
-        const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
+        const float w = s < p.k ? gates[tok * p.k + s] : 1.0f;
         p.slots[static_cast<size_t>(pair) * d + n0 + (lane & 15)] = w * (acc[i] + half_acc[slice][lane][i]);
       }
     }

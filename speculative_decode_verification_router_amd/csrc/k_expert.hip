@@ -5,7 +5,9 @@
 // the MFMA A operand.  Small batches skip the separate grouping kernel: every
 // wavefront of a gate/up block finds its block's tile from the routing
 // itself, and the blocks of the first slice pair write the grouping for the
-// down kernel, each its own tile's entry.
+// down kernel, each its own tile's entry.  Batches of up to 16 rows routed to
+// logits run gate/up and down in one launch (k_ffn_small), taking the top-k
+// in every block.
 #include "expert_core.h"
 
 namespace mv {
@@ -32,19 +34,41 @@ __device__ __forceinline__ bool table_tile(const ExpertArgs &p, int y, TileInfo 
 // segments and first tiles (shared expert s: segment T*k + s*T), a ballot
 // finds the expert whose tiles hold y, and the tile's rows are that expert's
 // pairs ranked by ballots in ascending pair order: the stable grouping.
-struct SmallTiles {
+struct alignas(16) SmallTiles {
   int cnt[kThreads / kWave][kWave];
   int rows[kThreads / kWave][kTileM];  // pair id (t*nslot + slot) of each tile row
+  // top-k from router logits (T <= kLogitsMaxT)
+  int ids[kLogitsMaxT * kMaxTopK];
+  float gates[kLogitsMaxT * kMaxTopK];
+  uint64_t keys[kThreads / kWave][kWave];
+  float sel[kThreads / kWave][kMaxTopK];
 };
 constexpr int kIdLoads = (kSmallT * kMaxTopK + kWave - 1) / kWave;  // id loads per lane
 
-__device__ bool small_tile(const ExpertArgs &p, int y, TileInfo &ti, SmallTiles &st, bool write_record) {
+// Top-k of every row from the router logits: wavefront w takes rows w, w+4,
+// ...; ids and gates go to LDS, and with write_record also to ids_out and
+// gates_out.  Synchronises the block.
+__device__ void small_top_k(const ExpertArgs &p, SmallTiles &st, bool write_record) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1), k = p.k;
+  for (int t = w; t < p.T; t += kThreads / kWave)
+    select_top_k(p.logits + static_cast<size_t>(t) * 64, st.keys[w], st.sel[w], p.E, k, st.ids + t * k,
+                 st.gates + t * k);
+  __syncthreads();
+  if (write_record && w == 0)
+    for (int i = lane; i < p.T * k; i += kWave) {
+      p.ids_out[i] = st.ids[i];
+      p.gates_out[i] = st.gates[i];
+    }
+}
+
+__device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo &ti, SmallTiles &st,
+                           bool write_record) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int E = p.E, S = p.S, k = p.k, T = p.T, np = T * k, ne = E + S;
   const uint64_t below = (1ull << lane) - 1ull;
   int v[kIdLoads];
 #pragma unroll
-  for (int i = 0; i < kIdLoads; ++i) v[i] = p.ids[min(i * kWave + lane, np - 1)];
+  for (int i = 0; i < kIdLoads; ++i) v[i] = ids[min(i * kWave + lane, np - 1)];
   int *cnt = st.cnt[w];
   cnt[lane] = 0;
 #pragma unroll
@@ -116,7 +140,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   constexpr int VN = Vec<T>::N;
   TileInfo ti;
   const bool small = p.group_in_block != 0;
-  if (small ? !small_tile(p, blockIdx.y, ti, st, blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kWave)
+  const bool first = blockIdx.x == 0 && blockIdx.y == 0;
+  if (small ? !small_tile(p, p.ids, blockIdx.y, ti, st, first && threadIdx.x < kWave)
             : !table_tile(p, blockIdx.y, ti))
     return;
   GateUpPart<T> part;
@@ -156,7 +181,95 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
   __syncthreads();
   const int lane = threadIdx.x & 63;
   part.finish(p, ti, reinterpret_cast<const T *>(smem) + (lane & 15) * (p.F + VN) + (lane >> 4) * VN, half_acc,
-              threadIdx.x);
+              threadIdx.x, p.rows + ti.r0, p.gates);
+}
+
+// ------------------------------------------- gate/up and down in one launch
+//
+// Batches routed to logits (up to kLogitsMaxT rows) run a layer's gate/up
+// and down in one launch.  The grid holds the gate/up blocks first, then the
+// down blocks, each tile-major; every block takes the top-k and finds its
+// tile itself.  A gate/up block writes its SiLU products with write-through
+// stores and, once they have completed, counts itself on its tile's counter.
+// A down block requests its first weight batch, waits until every gate/up
+// block of its tile has counted, and reads the products with agent-scope
+// loads.  A down block only waits for blocks of lower index, dispatched
+// before it; the wait is bounded, and a timeout is recorded in *err.
+constexpr int kSpinLimit = 1 << 18;  // polls of about a microsecond each
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_tiles) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ SmallTiles st;
+  __shared__ float xacc[2][64][4];
+  __shared__ int ready;
+  constexpr int VN = Vec<T>::N;
+  const int d = p.d, F = p.F, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sp_gu = (F + 31) / 32, sp_dn = (d + 31) / 32;
+  const bool gu = static_cast<int>(blockIdx.x) < sp_gu * max_tiles;
+  const int b = gu ? blockIdx.x : blockIdx.x - sp_gu * max_tiles;
+  const int sp = gu ? sp_gu : sp_dn, y = b / sp, pair = b - y * sp;
+  const bool first = blockIdx.x == 0;
+  small_top_k(p, st, first);
+  TileInfo ti;
+  if (!small_tile(p, st.ids, y, ti, st, first && tid < kWave)) return;
+  // LDS tile: rows [0, R) hold the tile's rows (R = min(T, 16) >= m), row R
+  // is zero and stands in for the MFMA rows past m
+  const int R = min(p.T, kTileM);
+  T *A = reinterpret_cast<T *>(smem);
+  const int arow = (lane & 15) < ti.m ? (lane & 15) : R;
+
+  if (gu) {
+    GateUpPart<T> part;
+    part.begin(p, ti, pair, tid);
+    const int nvec = d / VN, lda = d + VN;
+    const T *x = static_cast<const T *>(p.x);
+    for (int it = tid; it < (R + 1) * nvec; it += blockDim.x) {
+      const int rr = it / nvec, c = it - rr * nvec;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rr < ti.m) v = ld16(x + static_cast<size_t>(st.rows[w][rr] / p.nslot) * d + c * VN);
+      if (rr < ti.m || rr == R) st16(A + rr * lda + c * VN, v);
+    }
+    __syncthreads();
+    part.template finish<true>(p, ti, A + arow * lda + (lane >> 4) * VN, xacc, tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's products have completed
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(p.tile_done + y * kDoneStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
+  if (tid == 0) {  // no weight requests before the tile is ready: the wait takes no bandwidth
+    unsigned n = 0;
+    int polls = 0;
+    while ((n = __hip_atomic_load(p.tile_done + y * kDoneStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+               static_cast<unsigned>(sp_gu) &&
+           ++polls < kSpinLimit)
+      __builtin_amdgcn_s_sleep(64);
+    ready = n >= static_cast<unsigned>(sp_gu);
+    if (!ready) __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  DownPart<T> part;
+  part.begin(p, ti, pair, tid, p.w_routed_down, p.w_shared_down);
+  {  // the tile's products (agent-scope loads: written by this launch) and the zero row
+    const int nvec = F / VN, lda = F + VN;
+    const T *a = static_cast<const T *>(p.a);
+    for (int it = tid; it < (R + 1) * nvec; it += blockDim.x) {
+      const int rr = it / nvec, c = it - rr * nvec;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rr < ti.m) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(a + static_cast<size_t>(ti.r0 + rr) * F + c * VN);
+        v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (rr < ti.m || rr == R) st16(A + rr * lda + c * VN, v);
+    }
+  }
+  __syncthreads();
+  part.finish(p, ti, A + arow * (F + VN) + (lane >> 4) * VN, xacc, tid, st.rows[w], st.gates);
 }
 
 // ------------------------------------------------------------ medium batches
@@ -306,6 +419,22 @@ hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStre
   } else {
     allow_lds(k_gate_up<float>, smem);
     hipLaunchKernelGGL(k_gate_up<float>, grid, dim3(kThreads), smem, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  if (!a.logits || a.T > kLogitsMaxT || !a.tile_done || !a.err || !a.w_routed_down) return hipErrorInvalidValue;
+  const dim3 grid(((a.F + 31) / 32 + (a.d + 31) / 32) * max_tiles);
+  const size_t es = dtype == 1 ? 2 : 4;
+  const size_t rows = (a.T < kTileM ? a.T : kTileM) + 1;  // the tile's rows and a zero row
+  const size_t smem = rows * ((a.d > a.F ? a.d : a.F) + 16 / es) * es;
+  if (dtype == 1) {
+    allow_lds(k_ffn_small<bf16_t>, smem);
+    hipLaunchKernelGGL(k_ffn_small<bf16_t>, grid, dim3(kThreads), smem, s, a, max_tiles);
+  } else {
+    allow_lds(k_ffn_small<float>, smem);
+    hipLaunchKernelGGL(k_ffn_small<float>, grid, dim3(kThreads), smem, s, a, max_tiles);
   }
   return hipGetLastError();
 }

@@ -15,11 +15,17 @@ namespace mv {
 
 namespace {
 
+// kLogits: blocks (token, expert group), the groups of a token adjacent.
+__host__ __device__ inline int route_groups(const RouteArgs &a) {
+  return a.mode == kLogits ? (a.E + kRouteGroup - 1) / kRouteGroup : 1;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, CombineArgs c, int ntok) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int t0 = blockIdx.x * ntok;
-  route_block<T>(a, c, t0, min(ntok, a.T - t0), ntok, smem);
+  const int G = route_groups(a);
+  const int t0 = blockIdx.x / G * ntok;
+  route_block<T>(a, c, t0, min(ntok, a.T - t0), ntok, smem, blockIdx.x % G);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void k_group(RouteArgs a) {
@@ -104,7 +110,8 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
                              : reinterpret_cast<const void *>(k_route<float>);
   if (smem > 48 * 1024)
     (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-  const dim3 grid((a.T + ntok - 1) / ntok);
+  if (a.mode == kLogits && ntok != 1) return hipErrorInvalidValue;
+  const dim3 grid((a.T + ntok - 1) / ntok * route_groups(a));
   if (dtype == 1)
     hipLaunchKernelGGL(k_route<bf16_t>, grid, dim3(kRouteThreads), smem, s, a, c, ntok);
   else

@@ -31,7 +31,16 @@ enum RouteMode {
   kRoute = 0,    // RMSNorm -> router -> top-k (-> permutation)
   kFinal = 1,    // final RMSNorm -> x_f; clears the argmax keys
   kCombine = 2,  // combine only
+  kLogits = 3,   // RMSNorm -> router logits of one group of experts per block;
+                 // the top-k is left to the small-batch gate/up kernel
 };
+// Experts per routing block in kLogits mode, and the largest batch that
+// routes that way (every gate/up block then takes the top-k of all rows).
+constexpr int kRouteGroup = 16;
+constexpr int kLogitsMaxT = 16;
+// Per-tile counters of the fused expert launch, one per 256-byte line so
+// that polls of different tiles do not meet in one memory channel.
+constexpr int kDoneStride = 64;
 
 struct RouteArgs {
   int T, d, E, S, k, nslot, mode;
@@ -47,6 +56,9 @@ struct RouteArgs {
   int4 *tile_info;          // [max tiles] (expert, first row, rows, 0) per 16-row tile
   unsigned long long *argkey;  // kFinal: cleared
   unsigned *done;           // kFinal: cleared (the LM head's block count)
+  float *logits;            // kLogits: [T, 64] fp32 router logits
+  unsigned *tile_done;      // kLogits: counters [i * kDoneStride], i < n_tile_done, cleared for the fused expert launch
+  int n_tile_done;
 };
 
 // Combine of the previous layer's expert slots into the hidden state.
@@ -70,6 +82,15 @@ struct ExpertArgs {
   int4 *tile_info;         // [max tiles] (expert, first row, rows, 0)
   const float *gates;      // [T, k]
   float *slots;            // [T*nslot, d]
+  // kLogits routing (T <= kLogitsMaxT): the gate/up kernel takes the top-k of
+  // these logits itself, and its block (0, 0) writes ids_out and gates_out
+  const float *logits;     // [T, 64] or null
+  int *ids_out;            // [T, k]
+  float *gates_out;        // [T, k] (the down kernel's gates)
+  const void *w_routed_down;  // fused launch: this layer's down blocks ([E, d, F] and [S, d, F])
+  const void *w_shared_down;
+  unsigned *tile_done;     // [max tiles * kDoneStride] gate/up blocks done per tile (fused launch; zeroed by the routing)
+  unsigned *err;           // set to 1 if a fused launch's wait timed out
 };
 
 struct AcceptArgs {
@@ -95,6 +116,7 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 int gemm_tile_rows();

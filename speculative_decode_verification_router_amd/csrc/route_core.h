@@ -134,9 +134,12 @@ __host__ __device__ inline RouteSmem route_smem(int ntok, int d, int elem_bytes)
 }
 
 // Routes tokens [t0, t0 + nt) (nt <= ntok) with one block of kRouteThreads.
+// In kLogits mode the block takes expert group `eg` (experts kRouteGroup*eg
+// onwards) of one token and writes only their logits; group 0 also writes
+// h_dst and x_out.
 template <typename T>
 __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, int nt, int ntok,
-                            unsigned char *smem) {
+                            unsigned char *smem, int eg = 0) {
   constexpr int VN = Vec<T>::N;
   const int d = a.d, nvec = d / VN, ld = d + VN;
   const RouteSmem L = route_smem(ntok, d, sizeof(T));
@@ -151,8 +154,16 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   // Every load of the first phase is requested before any is used, so the
   // block waits on one memory round trip: the router weights, gamma, the rows
   // and all of their slots.
+  const bool logits_only = a.mode == kLogits;
+  const int e_blk = logits_only ? kRouteGroup * eg : 0;                  // first expert of this block
+  const int n_blk = logits_only ? kRouteGroup : 64;                      // experts of this block
+  const bool router_wave = 4 * wv < n_blk && e_blk + 4 * wv < a.E;       // four experts per wavefront
+  const bool writer = eg == 0;                                           // h_dst and x_out
+  if (logits_only && blockIdx.x == 0)
+    for (int i = tid; i < a.n_tile_done; i += blockDim.x) a.tile_done[i * kDoneStride] = 0u;
   uint4 wq[kRouterChunks];
-  if (a.mode == kRoute) router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, 4 * wv, d);
+  if ((a.mode == kRoute || logits_only) && router_wave)
+    router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, e_blk + 4 * wv, d);
   T *gl = reinterpret_cast<T *>(smem + L.g);
   uint4 gv = make_uint4(0, 0, 0, 0);
   if (a.mode != kCombine && tid < nvec) gv = ld16(static_cast<const T *>(a.gamma) + tid * VN);
@@ -213,7 +224,7 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
     }
     const uint2 pk = pack8(h, T());
     st8(hl + r * ld + col, pk);
-    if (c.slots && c.h_dst) st8(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + col, pk);
+    if (c.slots && c.h_dst && writer) st8(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + col, pk);
   }
   if (a.mode == kCombine) return;
   if (tid < nvec) st16(gl + tid * VN, gv);
@@ -241,7 +252,7 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
     for (int i = 0; i < VN; ++i) x[i] = round_to<T>((hv[i] * s) * g[i]);
     const uint4 pk = pack(x, T());
     st16(hl + r * ld + ch * VN, pk);
-    st16(xo + static_cast<size_t>(t0 + r) * d + ch * VN, pk);
+    if (writer) st16(xo + static_cast<size_t>(t0 + r) * d + ch * VN, pk);
   }
   if (a.mode == kFinal) {
     if (tid < nt) a.argkey[t0 + tid] = 0ull;
@@ -250,7 +261,13 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   }
   __syncthreads();
 
-  if (4 * wv < a.E)
+  if (logits_only) {
+    if (router_wave)
+      router_rows<T>(wq, hl, ld, nt, d, static_cast<const T *>(a.router_w), a.router_b, a.E, e_blk + 4 * wv,
+                     a.logits + static_cast<size_t>(t0) * 64);
+    return;
+  }
+  if (router_wave)
     router_rows<T>(wq, hl, ld, nt, d, static_cast<const T *>(a.router_w), a.router_b, a.E, 4 * wv, lg);
   __syncthreads();
   for (int r = wv; r < nt; r += blockDim.x / kWave)

@@ -294,26 +294,29 @@ def test_deterministic_and_batch_invariant(bd, torch_cuda, big):
 
 @pytest.mark.parametrize("model_name", ["tiny", "big"])
 def test_same_results_on_every_batch_path(bd, torch_cuda, tiny, big, model_name):
-    """Batches of up to 64 rows group the pairs inside the expert kernels,
-    up to 128 rows in a grouping kernel, and larger batches use 64-row expert
-    tiles.  All paths do the same per-row arithmetic in the same order, so a
-    sequence's results are bit-identical whichever path its batch takes."""
+    """Batches of up to 16 rows route in expert groups and take the top-k in
+    the gate/up kernel, up to 64 rows group the pairs inside the expert
+    kernels, up to 128 rows in a grouping kernel, and larger batches use
+    64-row expert tiles.  All paths do the same per-row arithmetic in the same
+    order, so a sequence's results are bit-identical whichever path its batch
+    takes."""
     dims, W, model = tiny if model_name == "tiny" else big
     K = 3
     n_seq = 33
     h = synth.make_hidden(dims, n_seq * (K + 1), seed=91)
     drafts = np.random.default_rng(2).integers(0, dims.vocab, (n_seq, K)).astype(np.int32)
+    batches = (1, 2, 4, 16, 17, 33)
     runs = {B: bd.run_verify_step(model, _dev(bd, h[:B * (K + 1)]), _dev(bd, drafts[:B]), B, K,
                                   routing=True)
-            for B in (16, 17, 33)}
+            for B in batches}
     _sync(torch_cuda)
-    small = runs[16]
-    for B in (17, 33):
-        other = runs[B]
+    ref = runs[batches[-1]]
+    for B in batches[:-1]:
+        run, T = runs[B], B * (K + 1)
         for key in ("h_out", "argmax", "committed", "n_committed"):
-            n = 16 if key in ("committed", "n_committed") else 64
-            assert np.array_equal(_host(bd, small[key]), _host(bd, other[key])[:n]), (B, key)
-        assert np.array_equal(_host(bd, small["topk_ids"]), _host(bd, other["topk_ids"])[:, :64]), B
+            n = B if key in ("committed", "n_committed") else T
+            assert np.array_equal(_host(bd, run[key])[:n], _host(bd, ref[key])[:n]), (B, key)
+        assert np.array_equal(_host(bd, run["topk_ids"]), _host(bd, ref["topk_ids"])[:, :T]), B
 
 
 def test_lossless_gpu_decode_loop(bd, torch_cuda, tiny):
