@@ -61,8 +61,9 @@ __device__ void small_top_k(const ExpertArgs &p, SmallTiles &st, bool write_reco
     }
 }
 
+// routed_only: y counts routed tiles only.
 __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo &ti, SmallTiles &st,
-                           bool write_record) {
+                           bool write_record, bool routed_only = false) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int E = p.E, S = p.S, k = p.k, T = p.T, np = T * k, ne = E + S;
   const uint64_t below = (1ull << lane) - 1ull;
@@ -100,7 +101,7 @@ __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo 
       p.tile_start[E + lane] = routed_tiles + lane * shared_tiles;
     }
   }
-  if (y >= routed_tiles + S * shared_tiles) return false;
+  if (y >= routed_tiles + (routed_only ? 0 : S * shared_tiles)) return false;
   int *rows = st.rows[w];
   if (y < routed_tiles) {
     const uint64_t hit = __ballot(lane < E && y >= first_e && y < first_e + tiles);
@@ -188,8 +189,9 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
 //
 // Batches routed to logits (up to kLogitsMaxT rows) run a layer's gate/up
 // and down in one launch.  The grid holds the gate/up blocks first, then the
-// down blocks, each tile-major; every block takes the top-k and finds its
-// tile itself.  A gate/up block writes its SiLU products with write-through
+// down blocks, each tile-major with the shared experts' tiles first (they
+// need no routing); every other block takes the top-k and finds its tile
+// itself.  A gate/up block writes its SiLU products with write-through
 // stores and, once they have completed, counts itself on its tile's counter.
 // A down block requests its first weight batch, waits until every gate/up
 // block of its tile has counted, and reads the products with agent-scope
@@ -209,10 +211,24 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
   const bool gu = static_cast<int>(blockIdx.x) < sp_gu * max_tiles;
   const int b = gu ? blockIdx.x : blockIdx.x - sp_gu * max_tiles;
   const int sp = gu ? sp_gu : sp_dn, y = b / sp, pair = b - y * sp;
-  const bool first = blockIdx.x == 0;
-  small_top_k(p, st, first);
+  // tiles [0, n_sh) are the shared experts' (all rows, no routing needed, so
+  // their weights are requested at once); routed tiles follow
+  const int shared_tiles = (p.T + kTileM - 1) / kTileM, n_sh = p.S * shared_tiles;
   TileInfo ti;
-  if (!small_tile(p, st.ids, y, ti, st, first && tid < kWave)) return;
+  if (y < n_sh) {
+    const int s = y / shared_tiles, j = y - s * shared_tiles;
+    ti.e = p.E + s;
+    ti.r0 = p.T * p.k + s * p.T + j * kTileM;
+    ti.m = min(kTileM, p.T - j * kTileM);
+    if (lane < ti.m) st.rows[w][lane] = (j * kTileM + lane) * p.nslot + p.k + s;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    const bool record = gu && y == n_sh && pair == 0;  // writes ids and gates of record
+    small_top_k(p, st, record);
+    if (!small_tile(p, st.ids, y - n_sh, ti, st, false, true)) return;
+  }
   // LDS tile: rows [0, R) hold the tile's rows (R = min(T, 16) >= m), row R
   // is zero and stands in for the MFMA rows past m
   const int R = min(p.T, kTileM);
