@@ -43,7 +43,9 @@ struct alignas(16) SmallTiles {
   uint64_t keys[kThreads / kWave][kWave];
   float sel[kThreads / kWave][kMaxTopK];
 };
-constexpr int kIdLoads = (kSmallT * kMaxTopK + kWave - 1) / kWave;  // id loads per lane
+// id loads per lane for up to kSmallT rows, and for the logits-routed batches
+constexpr int kIdLoads = (kSmallT * kMaxTopK + kWave - 1) / kWave;
+constexpr int kIdLoadsLogits = (kLogitsMaxT * kMaxTopK + kWave - 1) / kWave;
 
 // Top-k of every row from the router logits: wavefront w takes rows w, w+4,
 // ...; ids and gates go to LDS, and with write_record also to ids_out and
@@ -61,19 +63,20 @@ __device__ void small_top_k(const ExpertArgs &p, SmallTiles &st, bool write_reco
     }
 }
 
-// routed_only: y counts routed tiles only.
+// routed_only: y counts routed tiles only.  NL: id loads per lane (T*k <= 64*NL).
+template <int NL>
 __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo &ti, SmallTiles &st,
                            bool write_record, bool routed_only = false) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int E = p.E, S = p.S, k = p.k, T = p.T, np = T * k, ne = E + S;
   const uint64_t below = (1ull << lane) - 1ull;
-  int v[kIdLoads];
+  int v[NL];
 #pragma unroll
-  for (int i = 0; i < kIdLoads; ++i) v[i] = ids[min(i * kWave + lane, np - 1)];
+  for (int i = 0; i < NL; ++i) v[i] = ids[min(i * kWave + lane, np - 1)];
   int *cnt = st.cnt[w];
   cnt[lane] = 0;
 #pragma unroll
-  for (int i = 0; i < kIdLoads; ++i) {
+  for (int i = 0; i < NL; ++i) {
     v[i] = min(max(v[i], 0), E - 1);  // ids are always in range; clamp defensively
     if (i * kWave + lane < np) atomicAdd(&cnt[v[i]], 1);
   }
@@ -112,7 +115,7 @@ __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo 
     ti.m = min(kTileM, __builtin_amdgcn_readlane(c, e) - j * kTileM);
     int run = 0;  // pairs of expert e before this batch of 64
 #pragma unroll
-    for (int i = 0; i < kIdLoads; ++i) {
+    for (int i = 0; i < NL; ++i) {
       const int q = i * kWave + lane;
       const bool mine = q < np && v[i] == e;
       const uint64_t m = __ballot(mine);
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   TileInfo ti;
   const bool small = p.group_in_block != 0;
   const bool first = blockIdx.x == 0 && blockIdx.y == 0;
-  if (small ? !small_tile(p, p.ids, blockIdx.y, ti, st, first && threadIdx.x < kWave)
+  if (small ? !small_tile<kIdLoads>(p, p.ids, blockIdx.y, ti, st, first && threadIdx.x < kWave)
             : !table_tile(p, blockIdx.y, ti))
     return;
   GateUpPart<T> part;
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
   } else {
     const bool record = gu && y == n_sh && pair == 0;  // writes ids and gates of record
     small_top_k(p, st, record);
-    if (!small_tile(p, st.ids, y - n_sh, ti, st, false, true)) return;
+    if (!small_tile<kIdLoadsLogits>(p, st.ids, y - n_sh, ti, st, false, true)) return;
   }
   // LDS tile: rows [0, R) hold the tile's rows (R = min(T, 16) >= m), row R
   // is zero and stands in for the MFMA rows past m

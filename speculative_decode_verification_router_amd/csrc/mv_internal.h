@@ -10,10 +10,10 @@ namespace mv {
 // Rows of one expert tile of the grouped expert kernels, and tokens of one
 // routing tile.
 constexpr int kTileM = 16;
-// Up to this many token rows a step takes the small-batch path: one routing
-// block per token, and every gate/up block groups the (token, slot) pairs by
-// expert itself instead of a separate grouping kernel.
-constexpr int kSmallT = 64;
+// Up to this many token rows a step takes the small-batch path: every gate/up
+// block finds its tile from the routing itself instead of a separate
+// grouping kernel.
+constexpr int kSmallT = 128;
 // Batches of more than kMidMinT rows: expert tiles of up to kMidRows rows,
 // each weight row streamed once per tile (up to kMidMinT rows, 16-row tiles
 // with more wavefronts in flight stream faster).
