@@ -55,7 +55,8 @@ int max_tiles(const mv_config &c, int T, int tm) {
 int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T)); }
 
 struct Layout {
-  size_t hbuf, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, logits, tdone, total;
+  size_t hbuf, hbuf2, hbuf3, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, logits, tdone,
+      total;
 };
 
 Layout layout(const mv_config &c, int T) {
@@ -70,6 +71,9 @@ Layout layout(const mv_config &c, int T) {
     return at;
   };
   L.hbuf = take(static_cast<size_t>(T) * c.d_model * es);
+  // the combines of a verify step alternate between hidden-state buffers
+  L.hbuf2 = take(static_cast<size_t>(T) * c.d_model * es);
+  L.hbuf3 = take(static_cast<size_t>(T) * c.d_model * es);
   L.x = take(static_cast<size_t>(T) * c.d_model * es);
   L.ids = take(static_cast<size_t>(T) * c.top_k * 4);
   L.gates = take(static_cast<size_t>(T) * c.top_k * 4);
@@ -347,6 +351,7 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
   const int L = cfg->n_layers, k = cfg->top_k;
   float *gates = st.gates();
   const bool gemm = st.gemm();
+  const void *cur = h_in;  // hidden state entering the next combine (small and medium paths)
   for (int layer = 0; layer < L; ++layer) {
     int *ids = dbg_topk_ids ? dbg_topk_ids + static_cast<size_t>(layer) * T * k
                             : reinterpret_cast<int *>(st.ws + st.L.ids);
@@ -357,18 +362,25 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
         return rc;
       continue;
     }
-    // layer 0 routes h_in; later layers first add the previous layer's experts
+    // layer 0 routes h_in; later layers first add the previous layer's
+    // experts.  Logits routing runs several blocks per token that all read the
+    // row one of them writes, so each combine writes a buffer other than the
+    // one it reads (the final one, one block per token, may stay in place).
     const bool lg = st.logits_route();
-    if (layer == 0)
+    if (layer == 0) {
       rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, lg);
-    else
-      rc = st.route(layer, mv::kRoute, layer == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, ids, gates, lg);
+    } else {
+      void *dst = (L - layer) % 2 == 0 ? hbuf : static_cast<void *>(st.ws + st.L.hbuf2);
+      if (dst == cur) dst = st.ws + st.L.hbuf3;
+      rc = st.route(layer, mv::kRoute, cur, dst, st.slots(), nullptr, ids, gates, lg);
+      cur = dst;
+    }
     if (rc || (rc = st.ffn(layer, ids, gates, nullptr, nullptr, nullptr, lg))) return rc;
   }
   if (gemm)
     rc = st.route(L - 1, mv::kFinal, hbuf, nullptr, nullptr, nullptr, nullptr, nullptr);
   else
-    rc = st.route(L - 1, mv::kFinal, L == 1 ? h_in : hbuf, hbuf, st.slots(), nullptr, nullptr, nullptr);
+    rc = st.route(L - 1, mv::kFinal, cur, hbuf, st.slots(), nullptr, nullptr, nullptr);
   if (rc) return rc;
 
   // LM head; its last block to finish applies the accept rule
