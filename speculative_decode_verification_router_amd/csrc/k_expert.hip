@@ -196,9 +196,9 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
 // need no routing); every other block takes the top-k and finds its tile
 // itself.  A gate/up block writes its SiLU products with write-through
 // stores and, once they have completed, counts itself on its tile's counter.
-// A down block requests its first weight batch, waits until every gate/up
-// block of its tile has counted, and reads the products with agent-scope
-// loads.  A down block only waits for blocks of lower index, dispatched
+// A down block waits, without requesting anything else, until every gate/up
+// block of its tile has counted; then it requests its weights and reads the
+// products with agent-scope loads.  A down block only waits for blocks of lower index, dispatched
 // before it; the wait is bounded, and a timeout is recorded in *err.
 constexpr int kSpinLimit = 1 << 18;  // polls of about a microsecond each
 
