@@ -27,7 +27,7 @@ namespace {
 #ifndef MV_GEMM_BN
 #define MV_GEMM_BN 256
 #define MV_GEMM_BK 64
-#define MV_GEMM_PAD 16
+#define MV_GEMM_PAD 8
 #endif
 #ifndef MV_GEMM_WAVES_M
 #define MV_GEMM_WAVES_M 4
@@ -35,7 +35,10 @@ namespace {
 constexpr int kGBM = 256;             // rows per tile
 constexpr int kGBN = MV_GEMM_BN;      // B rows per block
 constexpr int kGBK = MV_GEMM_BK;      // K per LDS stage
-constexpr int kGLd = kGBK + MV_GEMM_PAD;  // LDS row stride in elements (no bank conflicts)
+// LDS row stride in elements: 144 bytes, nine 16-byte units, so the eight
+// rows one 16-byte read serves per cycle fall in distinct bank groups (the
+// rows are read 32 lanes deep by the MFMA fragments)
+constexpr int kGLd = kGBK + MV_GEMM_PAD;
 constexpr int kGWavesM = MV_GEMM_WAVES_M;  // wavefront grid: kGWavesM x kGWavesN bands
 constexpr int kGWavesN = kGBN / 128;
 constexpr int kGWaveM = kGBM / kGWavesM;  // rows per wavefront
