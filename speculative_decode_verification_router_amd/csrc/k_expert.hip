@@ -5,7 +5,7 @@
 // the MFMA A operand.  Small batches skip the separate grouping kernel: every
 // wavefront of a gate/up block finds its block's tile from the routing
 // itself, and the blocks of the first slice pair write the grouping for the
-// down kernel, each its own tile's entry.  Batches of up to 16 rows routed to
+// down kernel, each its own tile's entry.  Batches of up to 8 rows routed to
 // logits run gate/up and down in one launch (k_ffn_small), taking the top-k
 // in every block.
 #include "expert_core.h"

@@ -37,7 +37,7 @@ enum RouteMode {
 // Experts per routing block in kLogits mode, and the largest batch that
 // routes that way (every gate/up block then takes the top-k of all rows).
 constexpr int kRouteGroup = 16;
-constexpr int kLogitsMaxT = 16;
+constexpr int kLogitsMaxT = 8;  // measured: at 16 rows separate launches are 18% faster
 // Per-tile counters of the fused expert launch, one per 256-byte line so
 // that polls of different tiles do not meet in one memory channel.
 constexpr int kDoneStride = 64;

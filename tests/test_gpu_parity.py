@@ -294,7 +294,7 @@ def test_deterministic_and_batch_invariant(bd, torch_cuda, big):
 
 @pytest.mark.parametrize("model_name", ["tiny", "big"])
 def test_same_results_on_every_batch_path(bd, torch_cuda, tiny, big, model_name):
-    """Batches of up to 16 rows route in expert groups and take the top-k in
+    """Batches of up to 8 rows route in expert groups and take the top-k in
     the fused expert launch, up to 128 rows group the pairs inside the gate/up
     blocks, and larger batches use 64-row expert tiles after a grouping
     kernel.  All paths do the same per-row arithmetic in the same order, so a
