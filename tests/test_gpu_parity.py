@@ -40,6 +40,17 @@ def big(bd):
     return dims, W, bd.DeviceModel(dims, W, max_tokens=10048)
 
 
+@pytest.fixture(scope="module")
+def tiny3(bd):
+    """The tiny fp32 model with three layers: an odd layer count, so the first
+    combine of a verify step with h_out aliasing h_in would land on h_in."""
+    import dataclasses
+
+    dims = dataclasses.replace(synth.TINY_F32, n_layers=3)
+    W = synth.make_weights(dims, seed=4, gamma="uniform")
+    return dims, W, bd.DeviceModel(dims, W, max_tokens=64)
+
+
 def _dev(bd, a):
     return bd.to_device(a)
 
@@ -193,6 +204,31 @@ def test_verify_tiny_fp32(bd, torch_cuda, tiny):
     h = synth.workload_hidden(wl)
     _verify_check(bd, torch_cuda, dims, W, model, h, wl.batch, wl.k_draft, wl.match_p, 0,
                   "tiny verify")
+
+
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_verify_three_layers_in_place(bd, torch_cuda, tiny3, B):
+    """Three layers against the oracle; then the same step with h_out aliasing
+    h_in (the combines keep reading a buffer other than the one they write)
+    gives bit-identical results.  B = 1, 2 route to logits with the fused
+    expert launch, B = 4 the separate launches."""
+    dims, W, model = tiny3
+    K = 3
+    T = B * (K + 1)
+    h = synth.make_hidden(dims, T, seed=13)
+    _verify_check(bd, torch_cuda, dims, W, model, h, B, K, 0.6, 5, f"3-layer B={B}")
+    drafts = _dev(bd, np.random.default_rng(3).integers(0, dims.vocab, (B, K)).astype(np.int32))
+    ref = bd.run_verify_step(model, _dev(bd, h), drafts, B, K, routing=True)
+    torch = torch_cuda
+    ht = _dev(bd, h)
+    out = {key: torch.empty_like(ref[key])
+           for key in ("argmax", "n_accepted", "committed", "n_committed", "topk_ids")}
+    bd.moe_verify_step(model.cfg, model.weights, B, K, ht, drafts, ht, out["argmax"], out["n_accepted"],
+                       out["committed"], out["n_committed"], out["topk_ids"], model.ws, model.ws_bytes)
+    _sync(torch)
+    assert np.array_equal(_host(bd, ht), _host(bd, ref["h_out"]))
+    for key in out:
+        assert np.array_equal(_host(bd, out[key]), _host(bd, ref[key])), key
 
 
 @pytest.mark.parametrize("B,K", [(1, 0), (3, 1), (7, 3), (5, 15)])
