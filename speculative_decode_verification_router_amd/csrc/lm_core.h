@@ -8,7 +8,7 @@ namespace mv {
 
 constexpr int kLmWaves = 4;
 constexpr int kLmSlices = 4;   // 16-row vocabulary slices per wavefront
-constexpr int kLmUnroll = 8;
+constexpr int kLmUnroll = 16;
 constexpr int kLmRowsPerBlock = 16 * kLmSlices * kLmWaves;
 
 // Vocabulary block `vblk` (kLmRowsPerBlock rows: kLmWaves wavefronts of
