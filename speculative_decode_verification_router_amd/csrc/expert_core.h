@@ -20,7 +20,8 @@
 namespace mv {
 
 constexpr int kThreads = 256;  // 4 wavefronts
-constexpr int kUnroll = 8;     // K-windows whose loads are issued together
+constexpr int kUnroll = 8;       // K-windows whose loads are issued together
+constexpr int kUnrollFused = 20;  // the same in the fused small-batch launch (fewer, longer batches)
 
 struct TileInfo {
   int e, r0, m;
@@ -37,12 +38,12 @@ __device__ __forceinline__ const T *expert_base(const ExpertArgs &p, int e, size
   return expert_base<T>(p.w_routed, p.w_shared, p.E, e, elems);
 }
 
-// Weight loads of windows [w0, min(w0 + kUnroll, w_hi)) into registers.
-template <typename T>
+// Weight loads of windows [w0, min(w0 + U, w_hi)) into registers.
+template <typename T, int U = kUnroll>
 __device__ __forceinline__ void load_batch(uint4 *q, const T *b, int w0, int w_hi) {
   constexpr int W = 4 * Vec<T>::N;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
+  for (int u = 0; u < U; ++u)
     if (w0 + u < w_hi) q[u] = ld16(b + (w0 + u) * W);
 }
 
@@ -50,14 +51,14 @@ __device__ __forceinline__ void load_batch(uint4 *q, const T *b, int w0, int w_h
 // weights already in `q`: lane l reads A row (l % 16) from `a` (LDS) and B
 // column (l % 16) from `b` (global), both at K offset (l / 16) * VN inside
 // each window of 4*VN elements.
-template <typename T>
+template <typename T, int U = kUnroll>
 __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
                                            uint4 *q) {
   constexpr int W = 4 * Vec<T>::N;
-  for (int w0 = w_lo; w0 < w_hi; w0 += kUnroll) {
-    if (w0 != w_lo) load_batch<T>(q, b, w0, w_hi);
+  for (int w0 = w_lo; w0 < w_hi; w0 += U) {
+    if (w0 != w_lo) load_batch<T, U>(q, b, w0, w_hi);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
   }
 }
@@ -106,11 +107,11 @@ __device__ __forceinline__ void store_through(bf16_t *p, float v, int lane) {
 // gate/up of slice pair `pair` of a tile.  begin() issues the first weight
 // batch; finish() runs the MFMAs with this lane's A row at `arow` (LDS),
 // exchanges the up accumulators and writes a (one block barrier inside).
-template <typename T>
+template <typename T, int U = kUnroll>
 struct GateUpPart {
   const T *b;
   int f0, which, slice, nwin;
-  uint4 q[kUnroll];
+  uint4 q[U];
   __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid) {
     constexpr int VN = Vec<T>::N;
     const int lane = tid & 63, wv = tid >> 6;
@@ -121,7 +122,7 @@ struct GateUpPart {
     nwin = f0 < F ? d / (4 * VN) : 0;
     const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(2) * F * d);
     b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
-    load_batch<T>(q, b, 0, nwin);
+    load_batch<T, U>(q, b, 0, nwin);
   }
   // kThrough: a is written with write-through stores (read by other blocks
   // of the same launch).
@@ -130,7 +131,7 @@ struct GateUpPart {
                                          float (*up_acc)[64][4], int tid) {
     const int lane = tid & 63, F = p.F;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    mfma_panel<T>(acc, arow, b, 0, nwin, q);
+    mfma_panel<T, U>(acc, arow, b, 0, nwin, q);
     if (which == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) up_acc[slice][lane][i] = acc[i];
@@ -154,11 +155,11 @@ struct GateUpPart {
 
 // down of slice pair `pair` of a tile; same split as GateUpPart.  The down
 // weights are p.w_routed / p.w_shared unless given.
-template <typename T>
+template <typename T, int U = kUnroll>
 struct DownPart {
   const T *b;
   int n0, half, slice, w_lo, w_hi;
-  uint4 q[kUnroll];
+  uint4 q[U];
   __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid,
                                         const void *w_routed = nullptr, const void *w_shared = nullptr) {
     constexpr int VN = Vec<T>::N;
@@ -173,7 +174,7 @@ struct DownPart {
     const T *W = w_routed ? expert_base<T>(w_routed, w_shared, p.E, ti.e, static_cast<size_t>(d) * F)
                           : expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
     b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
-    load_batch<T>(q, b, w_lo, w_hi);
+    load_batch<T, U>(q, b, w_lo, w_hi);
   }
   // tile_rows[row]: the pair id (t*nslot + slot) of tile row `row`; gates:
   // [T, k] softmax gates of the routed pairs.
@@ -182,7 +183,7 @@ struct DownPart {
                                          const float *gates) {
     const int lane = tid & 63, d = p.d;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    mfma_panel<T>(acc, arow, b, w_lo, w_hi, q);
+    mfma_panel<T, U>(acc, arow, b, w_lo, w_hi, q);
     if (half == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) half_acc[slice][lane][i] = acc[i];

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
   const int arow = (lane & 15) < ti.m ? (lane & 15) : R;
 
   if (gu) {
-    GateUpPart<T> part;
+    GateUpPart<T, kUnrollFused> part;
     part.begin(p, ti, pair, tid);
     const int nvec = d / VN, lda = d + VN;
     const T *x = static_cast<const T *>(p.x);
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
     if (!ready) __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  DownPart<T> part;
+  DownPart<T, kUnrollFused> part;
   part.begin(p, ti, pair, tid, p.w_routed_down, p.w_shared_down);
   {  // the tile's products (agent-scope loads: written by this launch) and the zero row
     const int nvec = F / VN, lda = F + VN;
