@@ -59,6 +59,12 @@ struct Layout {
       total;
 };
 
+// Words of one set of fused-launch counters: one per tile and one per copy of
+// the routing counter, each on its own 256-byte line.
+size_t done_set_words(const mv_config &c, int T) {
+  return (static_cast<size_t>(max_tiles(c, T, mv::kTileM)) + mv::kRouteCopies) * mv::kDoneStride;
+}
+
 Layout layout(const mv_config &c, int T) {
   const size_t es = c.dtype == MV_BF16 ? 2 : 4;
   const size_t nslot = static_cast<size_t>(c.top_k + c.n_shared);
@@ -88,7 +94,8 @@ Layout layout(const mv_config &c, int T) {
   L.done = take(4);
   L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
   L.logits = take(static_cast<size_t>(T) * 64 * 4);
-  L.tdone = take((static_cast<size_t>(max_tiles(c, T, mv::kTileM)) + 1) * mv::kDoneStride * 4);  // + the timeout word
+  // two sets of fused-launch counters (tiles, then the routing copies), then the timeout word
+  L.tdone = take((2 * done_set_words(c, T) + mv::kDoneStride) * 4);
   L.total = off;
   return L;
 }
@@ -206,7 +213,12 @@ struct Step {
   // Router logits spread over expert groups, top-k in the gate/up kernel.
   bool logits_route() const { return T <= mv::kLogitsMaxT; }
   float *logits() const { return reinterpret_cast<float *>(ws + L.logits); }
-  unsigned *tile_done() const { return reinterpret_cast<unsigned *>(ws + L.tdone); }
+  // fused-launch counter set s (0 or 1): tile counters, then the routing copies
+  unsigned *done_set(int s) const {
+    return reinterpret_cast<unsigned *>(ws + L.tdone) + static_cast<size_t>(s) * done_set_words(c, T);
+  }
+  int done_count() const { return max_tiles(c, T, mv::kTileM) + mv::kRouteCopies; }
+  unsigned *done_err() const { return done_set(2); }
   // LDS-tiled GEMMs; the combine is in the shared experts' down projection
   bool gemm() const { return path_for(c, T) == kGemmTiles; }
 
@@ -217,11 +229,11 @@ struct Step {
   int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
             float *y_moe, int *ids, float *gates_out, bool logits = false) const {
     mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
-    if (logits && mode == mv::kRoute) {
+    if (logits && mode == mv::kRoute) {  // also clears counter set 0 for the first fused launch
       a.mode = mv::kLogits;
       a.logits = this->logits();
-      a.tile_done = tile_done();
-      a.n_tile_done = max_tiles(c, T, mv::kTileM);
+      a.tile_done = done_set(0);
+      a.n_tile_done = done_count();
     }
     if (mode == mv::kRoute && gemm()) {  // h_src is already combined on this path
       return hip_status(mv::launch_route_large(a, h_src, reinterpret_cast<int *>(ws + L.bcnt), s));
@@ -239,10 +251,13 @@ struct Step {
 
   // gate/up then down for `layer`, leaving the weighted expert outputs in
   // slots; on the GEMM path also the combine h_dst = h_src + y (y_moe: y).
-  // `logits`: the routing of this layer stopped at the logits; the gate/up
-  // kernel takes the top-k and writes ids and gates.
+  // `logits`: the routing of this layer stops at the logits (done by the
+  // routing kernel before, or with ra / ca inside this launch); the fused
+  // expert launch takes the top-k and writes ids and gates.  It uses counter
+  // set layer % 2 and clears the other one for the next layer.
   int ffn(int layer, int *ids, float *gates, const void *h_src = nullptr, void *h_dst = nullptr,
-          float *y_moe = nullptr, bool logits = false) const {
+          float *y_moe = nullptr, bool logits = false, const mv::RouteArgs *ra = nullptr,
+          const mv::CombineArgs *ca = nullptr) const {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e{};
     e.T = T;
@@ -270,11 +285,15 @@ struct Step {
       e.logits = this->logits();
       e.ids_out = ids;
       e.gates_out = gates;
-      e.tile_done = tile_done();
-      e.err = tile_done() + static_cast<size_t>(max_tiles(c, T, mv::kTileM)) * mv::kDoneStride;
+      const int set = layer % 2;
+      e.tile_done = done_set(set);
+      e.route_done = done_set(set) + static_cast<size_t>(max_tiles(c, T, mv::kTileM)) * mv::kDoneStride;
+      e.done_next = done_set(1 - set);
+      e.n_done = done_count();
+      e.err = done_err();
       e.w_routed_down = lp.down;
       e.w_shared_down = lp.sdown;
-      return hip_status(mv::launch_ffn_small(c.dtype, e, mt, s));
+      return hip_status(mv::launch_ffn_small(c.dtype, e, ra, ca, mt, s));
     }
     const Path path = path_for(c, T);
     int rc = hip_status(path == kGemmTiles  ? mv::launch_gemm_gate_up(e, mt, s)
@@ -366,16 +385,27 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
     // experts.  Logits routing runs several blocks per token that all read the
     // row one of them writes, so each combine writes a buffer other than the
     // one it reads (the final one, one block per token, may stay in place).
+    // Up to kLogitsMaxT rows, layers after the first route inside their
+    // fused expert launch.
     const bool lg = st.logits_route();
     if (layer == 0) {
       rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, lg);
-    } else {
-      void *dst = (L - layer) % 2 == 0 ? hbuf : static_cast<void *>(st.ws + st.L.hbuf2);
-      if (dst == cur) dst = st.ws + st.L.hbuf3;
-      rc = st.route(layer, mv::kRoute, cur, dst, st.slots(), nullptr, ids, gates, lg);
-      cur = dst;
+      if (rc || (rc = st.ffn(0, ids, gates, nullptr, nullptr, nullptr, lg))) return rc;
+      continue;
     }
-    if (rc || (rc = st.ffn(layer, ids, gates, nullptr, nullptr, nullptr, lg))) return rc;
+    void *dst = (L - layer) % 2 == 0 ? hbuf : static_cast<void *>(st.ws + st.L.hbuf2);
+    if (dst == cur) dst = st.ws + st.L.hbuf3;
+    if (lg) {
+      mv::RouteArgs ra = st.route_args(layer, mv::kRoute, ids, gates);
+      ra.mode = mv::kLogits;
+      ra.logits = st.logits();
+      const mv::CombineArgs cb{cur, dst, st.slots(), nullptr};
+      rc = st.ffn(layer, ids, gates, nullptr, nullptr, nullptr, true, &ra, &cb);
+    } else if (!(rc = st.route(layer, mv::kRoute, cur, dst, st.slots(), nullptr, ids, gates))) {
+      rc = st.ffn(layer, ids, gates);
+    }
+    if (rc) return rc;
+    cur = dst;
   }
   if (gemm)
     rc = st.route(L - 1, mv::kFinal, hbuf, nullptr, nullptr, nullptr, nullptr, nullptr);

@@ -53,8 +53,8 @@ constexpr int kIdLoadsLogits = (kLogitsMaxT * kMaxTopK + kWave - 1) / kWave;
 __device__ void small_top_k(const ExpertArgs &p, SmallTiles &st, bool write_record) {
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1), k = p.k;
   for (int t = w; t < p.T; t += kThreads / kWave)
-    select_top_k(p.logits + static_cast<size_t>(t) * 64, st.keys[w], st.sel[w], p.E, k, st.ids + t * k,
-                 st.gates + t * k);
+    select_top_k<true>(p.logits + static_cast<size_t>(t) * 64, st.keys[w], st.sel[w], p.E, k, st.ids + t * k,
+                       st.gates + t * k);
   __syncthreads();
   if (write_record && w == 0)
     for (int i = lane; i < p.T * k; i += kWave) {
@@ -202,23 +202,47 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
 // before it; the wait is bounded, and a timeout is recorded in *err.
 constexpr int kSpinLimit = 1 << 18;  // polls of about a microsecond each
 
+// Thread 0 waits (bounded) until *ctr >= target; a timeout is recorded in
+// *err.  The caller synchronises the block afterwards.
+__device__ __forceinline__ void wait_count(const unsigned *ctr, unsigned target, unsigned *err) {
+  if (threadIdx.x != 0) return;
+  unsigned n = 0;
+  int polls = 0;
+  while ((n = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target && ++polls < kSpinLimit)
+    __builtin_amdgcn_s_sleep(64);
+  if (n < target) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// n_route > 0: the launch also routes this layer (ra, ca): its first n_route
+// blocks (token, expert group) run route_fused, and the other blocks wait
+// for them (shared gate/up blocks after requesting their first weights).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_tiles) {
+__global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs ra, CombineArgs ca, int max_tiles,
+                                                        int n_route) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SmallTiles st;
   __shared__ float xacc[2][64][4];
-  __shared__ int ready;
   constexpr int VN = Vec<T>::N;
   const int d = p.d, F = p.F, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (blockIdx.x == 0)  // the next launch's counters (this launch's were cleared before it started)
+    for (int i = tid; i < p.n_done; i += blockDim.x) p.done_next[static_cast<size_t>(i) * kDoneStride] = 0u;
+  if (static_cast<int>(blockIdx.x) < n_route) {
+    const int G = (p.E + kRouteGroup - 1) / kRouteGroup;
+    route_fused<T>(ra, ca, blockIdx.x / G, blockIdx.x % G, smem, p.route_done, kRouteCopies, kDoneStride);
+    return;
+  }
+  const unsigned *route_ctr = p.route_done + static_cast<size_t>(blockIdx.x % kRouteCopies) * kDoneStride;
   const int sp_gu = (F + 31) / 32, sp_dn = (d + 31) / 32;
-  const bool gu = static_cast<int>(blockIdx.x) < sp_gu * max_tiles;
-  const int b = gu ? blockIdx.x : blockIdx.x - sp_gu * max_tiles;
+  const int b0 = blockIdx.x - n_route;
+  const bool gu = b0 < sp_gu * max_tiles;
+  const int b = gu ? b0 : b0 - sp_gu * max_tiles;
   const int sp = gu ? sp_gu : sp_dn, y = b / sp, pair = b - y * sp;
   // tiles [0, n_sh) are the shared experts' (all rows, no routing needed, so
   // their weights are requested at once); routed tiles follow
   const int shared_tiles = (p.T + kTileM - 1) / kTileM, n_sh = p.S * shared_tiles;
+  const bool shared = y < n_sh;
   TileInfo ti;
-  if (y < n_sh) {
+  if (shared) {
     const int s = y / shared_tiles, j = y - s * shared_tiles;
     ti.e = p.E + s;
     ti.r0 = p.T * p.k + s * p.T + j * kTileM;
@@ -228,6 +252,10 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   } else {
+    if (n_route) {
+      wait_count(route_ctr, n_route, p.err);
+      __syncthreads();
+    }
     const bool record = gu && y == n_sh && pair == 0;  // writes ids and gates of record
     small_top_k(p, st, record);
     if (!small_tile<kIdLoadsLogits>(p, st.ids, y - n_sh, ti, st, false, true)) return;
@@ -241,12 +269,27 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
   if (gu) {
     GateUpPart<T, kUnrollFused> part;
     part.begin(p, ti, pair, tid);
+    if (shared && n_route) {  // x is written by this launch's routing blocks
+      wait_count(route_ctr, n_route, p.err);
+      __syncthreads();
+    }
     const int nvec = d / VN, lda = d + VN;
     const T *x = static_cast<const T *>(p.x);
     for (int it = tid; it < (R + 1) * nvec; it += blockDim.x) {
       const int rr = it / nvec, c = it - rr * nvec;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (rr < ti.m) v = ld16(x + static_cast<size_t>(st.rows[w][rr] / p.nslot) * d + c * VN);
+      if (rr < ti.m) {
+        const T *src = x + static_cast<size_t>(st.rows[w][rr] / p.nslot) * d + c * VN;
+        if (n_route) {
+          const uint32_t *q = reinterpret_cast<const uint32_t *>(src);
+          v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          v = ld16(src);
+        }
+      }
       if (rr < ti.m || rr == R) st16(A + rr * lda + c * VN, v);
     }
     __syncthreads();
@@ -258,16 +301,8 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, int max_ti
     return;
   }
 
-  if (tid == 0) {  // no weight requests before the tile is ready: the wait takes no bandwidth
-    unsigned n = 0;
-    int polls = 0;
-    while ((n = __hip_atomic_load(p.tile_done + y * kDoneStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
-               static_cast<unsigned>(sp_gu) &&
-           ++polls < kSpinLimit)
-      __builtin_amdgcn_s_sleep(64);
-    ready = n >= static_cast<unsigned>(sp_gu);
-    if (!ready) __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // no weight requests before the tile is ready: the wait takes no bandwidth
+  wait_count(p.tile_done + y * kDoneStride, static_cast<unsigned>(sp_gu), p.err);
   __syncthreads();
   DownPart<T, kUnrollFused> part;
   part.begin(p, ti, pair, tid, p.w_routed_down, p.w_shared_down);
@@ -442,18 +477,29 @@ hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  if (!a.logits || a.T > kLogitsMaxT || !a.tile_done || !a.err || !a.w_routed_down) return hipErrorInvalidValue;
-  const dim3 grid(((a.F + 31) / 32 + (a.d + 31) / 32) * max_tiles);
+hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra, const CombineArgs *ca, int max_tiles,
+                            hipStream_t s) {
+  if (!a.logits || a.T > kLogitsMaxT || !a.tile_done || !a.route_done || !a.done_next || !a.err ||
+      !a.w_routed_down)
+    return hipErrorInvalidValue;
+  if (ra && (ra->mode != kLogits || ra->logits != a.logits)) return hipErrorInvalidValue;
+  const int n_route = ra ? a.T * ((a.E + kRouteGroup - 1) / kRouteGroup) : 0;
+  const dim3 grid(n_route + ((a.F + 31) / 32 + (a.d + 31) / 32) * max_tiles);
   const size_t es = dtype == 1 ? 2 : 4;
   const size_t rows = (a.T < kTileM ? a.T : kTileM) + 1;  // the tile's rows and a zero row
-  const size_t smem = rows * ((a.d > a.F ? a.d : a.F) + 16 / es) * es;
+  size_t smem = rows * ((a.d > a.F ? a.d : a.F) + 16 / es) * es;
+  if (ra) {
+    const size_t route = route_smem(1, a.d, static_cast<int>(es)).total;
+    smem = smem > route ? smem : route;
+  }
+  const RouteArgs r0 = ra ? *ra : RouteArgs{};
+  const CombineArgs c0 = ca ? *ca : CombineArgs{};
   if (dtype == 1) {
     allow_lds(k_ffn_small<bf16_t>, smem);
-    hipLaunchKernelGGL(k_ffn_small<bf16_t>, grid, dim3(kThreads), smem, s, a, max_tiles);
+    hipLaunchKernelGGL(k_ffn_small<bf16_t>, grid, dim3(kThreads), smem, s, a, r0, c0, max_tiles, n_route);
   } else {
     allow_lds(k_ffn_small<float>, smem);
-    hipLaunchKernelGGL(k_ffn_small<float>, grid, dim3(kThreads), smem, s, a, max_tiles);
+    hipLaunchKernelGGL(k_ffn_small<float>, grid, dim3(kThreads), smem, s, a, r0, c0, max_tiles, n_route);
   }
   return hipGetLastError();
 }

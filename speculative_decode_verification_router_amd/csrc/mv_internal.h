@@ -41,6 +41,9 @@ constexpr int kLogitsMaxT = 8;  // measured: at 16 rows separate launches are 18
 // Per-tile counters of the fused expert launch, one per 256-byte line so
 // that polls of different tiles do not meet in one memory channel.
 constexpr int kDoneStride = 64;
+// Copies of the routing counter of a fused launch that also routes, so that
+// its many waiting blocks spread their polls over that many lines.
+constexpr int kRouteCopies = 32;
 
 struct RouteArgs {
   int T, d, E, S, k, nslot, mode;
@@ -89,7 +92,12 @@ struct ExpertArgs {
   float *gates_out;        // [T, k] (the down kernel's gates)
   const void *w_routed_down;  // fused launch: this layer's down blocks ([E, d, F] and [S, d, F])
   const void *w_shared_down;
-  unsigned *tile_done;     // [max tiles * kDoneStride] gate/up blocks done per tile (fused launch; zeroed by the routing)
+  // fused launch: this launch's counters, one per 256-byte line (cleared
+  // before it starts), and the next launch's, which it clears
+  unsigned *tile_done;     // [tile * kDoneStride]: gate/up blocks done per tile
+  unsigned *route_done;    // [copy * kDoneStride]: routing blocks done, kRouteCopies copies
+  unsigned *done_next;     // [i * kDoneStride], i < n_done
+  int n_done;
   unsigned *err;           // set to 1 if a fused launch's wait timed out
 };
 
@@ -116,7 +124,9 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
-hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+// ra / ca: also route this layer inside the launch (kLogits), or null.
+hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra, const CombineArgs *ca, int max_tiles,
+                            hipStream_t s);
 hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 int gemm_tile_rows();

@@ -42,7 +42,9 @@ __device__ __forceinline__ void router_preload(uint4 *wq, const T *w_router, int
 }
 
 // Router logits of tokens [0, nt) of the x rows in LDS (x_lds[t*ldx + j]).
-template <typename T>
+// kThrough: the logits are written through (read by other blocks of the
+// same launch).
+template <typename T, bool kThrough = false>
 __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int ldx, int nt, int d,
                                             const T *w_router, const float *bias, int E, int e_base,
                                             float *lg) {
@@ -68,7 +70,10 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
     for (int c = q + 16 * kRouterChunks; c < nvec; c += 16) accumulate(ld16(wr + c * VN), c);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-    if (q == 0 && e < 64) lg[t * 64 + e] = acc + b;
+    if (q == 0 && e < 64) {
+      if constexpr (kThrough) __hip_atomic_store(lg + t * 64 + e, acc + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else lg[t * 64 + e] = acc + b;
+    }
   }
 }
 
@@ -76,11 +81,15 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
 // is the number of experts ordered before it by (logit desc, id asc).  Each
 // lane's (logit, id) key goes to LDS once (lanes >= E write 0, below every
 // real key) and every lane counts the keys above its own, two per read.
-// key_lds: 64 keys, 16-byte aligned; sel_lds: kMaxTopK floats.
+// key_lds: 64 keys, 16-byte aligned; sel_lds: kMaxTopK floats.  kCoherent:
+// the logits were written by other blocks of the same launch and are read
+// with agent-scope loads.
+template <bool kCoherent = false>
 __device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_lds, float *sel_lds, int E,
                                              int k, int *ids, float *gates) {
   const int lane = threadIdx.x & 63;
-  const float logit = lg_row[lane];
+  const float logit = kCoherent ? __hip_atomic_load(lg_row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : lg_row[lane];
   const uint64_t mine = lane < E ? argmax_key(logit, static_cast<uint32_t>(lane)) : 0ull;
   key_lds[lane] = mine;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -273,6 +282,114 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   for (int r = wv; r < nt; r += blockDim.x / kWave)
     select_top_k(lg + r * 64, keys + r * 64, sel + r * kMaxTopK, a.E, a.k, a.ids + (t0 + r) * a.k,
                  a.gates + (t0 + r) * a.k);
+}
+
+// Routing of one token inside the fused small-batch expert launch: a block of
+// 256 threads takes token t's combine and RMSNorm and the logits of expert
+// group eg.  The arithmetic is route_block's in kLogits mode, with one thread
+// per 16-byte chunk (its sum of squares is the same sequential sum).  x and
+// the logits, which other blocks of the launch read, are written through;
+// once they have completed, the block adds 1 to every copy of the routing
+// counter (done[i * stride], i < copies).  Group 0 also writes h_dst, which
+// only later launches read.
+template <typename T>
+__device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int eg, unsigned char *smem,
+                            unsigned *done, int copies, int stride) {
+  constexpr int VN = Vec<T>::N;
+  constexpr int kSlotBatch = 8;
+  const int d = a.d, nvec = d / VN;
+  const RouteSmem L = route_smem(1, d, sizeof(T));
+  T *hl = reinterpret_cast<T *>(smem + L.h);
+  T *gl = reinterpret_cast<T *>(smem + L.g);
+  float *pl = reinterpret_cast<float *>(smem + L.p);
+  float *inv = reinterpret_cast<float *>(smem + L.inv);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e_blk = kRouteGroup * eg;
+  const bool router_wave = 4 * wv < kRouteGroup && e_blk + 4 * wv < a.E;
+  const bool writer = eg == 0;
+
+  uint4 wq[kRouterChunks];
+  if (router_wave) router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, e_blk + 4 * wv, d);
+  const T *hs = static_cast<const T *>(c.h_src);
+  for (int ch = tid; ch < nvec; ch += blockDim.x) {
+    const uint4 gv = ld16(static_cast<const T *>(a.gamma) + ch * VN);
+    const T *hrow = hs + static_cast<size_t>(t) * d + ch * VN;
+    float h[VN];
+    if (c.slots) {
+      const float *sp = c.slots + static_cast<size_t>(t) * a.nslot * d + ch * VN;
+      float v[kSlotBatch][VN], y[VN];
+#pragma unroll
+      for (int s = 0; s < kSlotBatch; ++s)
+#pragma unroll
+        for (int i = 0; i < VN; i += 4) ld_f32<4>(sp + static_cast<size_t>(min(s, a.nslot - 1)) * d + i, v[s] + i);
+      const uint4 hq = ld16(hrow);
+#pragma unroll
+      for (int i = 0; i < VN; ++i) y[i] = 0.f + v[0][i];
+#pragma unroll
+      for (int s = 1; s < kSlotBatch; ++s)
+#pragma unroll
+        for (int i = 0; i < VN; ++i) y[i] += s < a.nslot ? v[s][i] : -0.f;
+      for (int s0 = kSlotBatch; s0 < a.nslot; s0 += kSlotBatch) {
+#pragma unroll
+        for (int s = 0; s < kSlotBatch; ++s)
+#pragma unroll
+          for (int i = 0; i < VN; i += 4)
+            ld_f32<4>(sp + static_cast<size_t>(min(s0 + s, a.nslot - 1)) * d + i, v[s] + i);
+#pragma unroll
+        for (int s = 0; s < kSlotBatch; ++s)
+#pragma unroll
+          for (int i = 0; i < VN; ++i) y[i] += s0 + s < a.nslot ? v[s][i] : -0.f;
+      }
+      unpack(hq, h, T());
+#pragma unroll
+      for (int i = 0; i < VN; ++i) h[i] = round_to<T>(h[i] + y[i]);
+    } else {
+      unpack(ld16(hrow), h, T());
+    }
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < VN; ++i) p += h[i] * h[i];
+    pl[ch] = p;
+    const uint4 pk = pack(h, T());
+    st16(hl + ch * VN, pk);
+    st16(gl + ch * VN, gv);
+    if (c.slots && c.h_dst && writer) st16(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + ch * VN, pk);
+  }
+  __syncthreads();
+  if (wv == 0) {  // sum of squares and 1/rms, in route_block's order
+    float acc = 0.f;
+    for (int ch = lane; ch < nvec; ch += kWave) acc += pl[ch];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) inv[0] = 1.0f / sqrtf(acc / static_cast<float>(d) + a.eps);
+  }
+  __syncthreads();
+  T *xo = static_cast<T *>(a.x_out) + static_cast<size_t>(t) * d;
+  for (int ch = tid; ch < nvec; ch += blockDim.x) {
+    float hv[VN], g[VN], x[VN];
+    unpack(ld16(hl + ch * VN), hv, T());
+    unpack(ld16(gl + ch * VN), g, T());
+    const float sc = inv[0];
+#pragma unroll
+    for (int i = 0; i < VN; ++i) x[i] = round_to<T>((hv[i] * sc) * g[i]);
+    const uint4 pk = pack(x, T());
+    st16(hl + ch * VN, pk);
+    if (writer) {
+      uint32_t *q = reinterpret_cast<uint32_t *>(xo + ch * VN);
+      __hip_atomic_store(q, pk.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, pk.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 2, pk.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 3, pk.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (router_wave)
+    router_rows<T, true>(wq, hl, 0, 1, d, static_cast<const T *>(a.router_w), a.router_b, a.E, e_blk + 4 * wv,
+                         a.logits + static_cast<size_t>(t) * 64);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's x and logits have completed
+  __syncthreads();
+  if (tid < copies)
+    __hip_atomic_fetch_add(done + static_cast<size_t>(tid) * stride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- grouping
