@@ -104,23 +104,31 @@ struct Stager {
 // Per wavefront: a kGWaveM x kGWaveN output band as kGMT x (kGWaveN / 32) tiles of 32x32.
 typedef f32x16_t GemmAcc[kGMT][kGWaveN / 32];
 
-// MFMAs of one K-step from LDS buffer `cur`.
+// MFMAs of one K-step from LDS buffer `cur`; the fragments of the next
+// 16-deep slice are read while the current one is multiplied.
 __device__ __forceinline__ void gemm_step(const GemmSmem &sm, int cur, GemmAcc &acc) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv % kGWavesM, wn = wv / kGWavesM;
   const bf16_t *as = sm.a[cur] + (wm * kGWaveM + (lane & 31)) * kGLd + (lane >> 5) * 8;
   const bf16_t *bs = sm.b[cur] + (wn * kGWaveN + (lane & 31)) * kGLd + (lane >> 5) * 8;
+  uint4 af[2][kGMT], bfr[2][kGWaveN / 32];
+#pragma unroll
+  for (int i = 0; i < kGMT; ++i) af[0][i] = ld16(as + i * 32 * kGLd);
+#pragma unroll
+  for (int j = 0; j < kGWaveN / 32; ++j) bfr[0][j] = ld16(bs + j * 32 * kGLd);
 #pragma unroll
   for (int u = 0; u < kGBK / 16; ++u) {
-    uint4 af[kGMT], bfr[kGWaveN / 32];
+    const int c = u & 1;
+    if (u + 1 < kGBK / 16) {
 #pragma unroll
-    for (int i = 0; i < kGMT; ++i) af[i] = ld16(as + i * 32 * kGLd + u * 16);
+      for (int i = 0; i < kGMT; ++i) af[c ^ 1][i] = ld16(as + i * 32 * kGLd + (u + 1) * 16);
 #pragma unroll
-    for (int j = 0; j < kGWaveN / 32; ++j) bfr[j] = ld16(bs + j * 32 * kGLd + u * 16);
+      for (int j = 0; j < kGWaveN / 32; ++j) bfr[c ^ 1][j] = ld16(bs + j * 32 * kGLd + (u + 1) * 16);
+    }
 #pragma unroll
     for (int i = 0; i < kGMT; ++i)
 #pragma unroll
-      for (int j = 0; j < kGWaveN / 32; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+      for (int j = 0; j < kGWaveN / 32; ++j) mfma32(acc[i][j], af[c][i], bfr[c][j]);
   }
 }
 
