@@ -80,7 +80,10 @@ __device__ bool gemm_item(const int *tile_start, int ne, int nb_count, int &tile
 
 // Global -> registers -> LDS copy of a [ROWS x kGBK] tile, kGChunks threads
 // per row; kStages steps are in flight in registers, one slot per step.
-constexpr int kStages = 2;
+#ifndef MV_GEMM_STAGES
+#define MV_GEMM_STAGES 2
+#endif
+constexpr int kStages = MV_GEMM_STAGES;
 
 template <int ROWS>
 struct Stager {
@@ -285,26 +288,46 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down(ExpertArgs p) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   gemm_mainloop<NK>(sm, A, B, F / kGBK, acc);
 
+  // the pair ids and gates of kEpi row tiles of this lane are read before
+  // their first store: loads and stores share one memory counter, so a gate
+  // read between stores would wait for all of them to complete
+  constexpr int kEpi = kGMT < 2 ? kGMT : 2;
 #pragma unroll
-  for (int i = 0; i < kGMT; ++i)
+  for (int i0 = 0; i0 < kGMT; i0 += kEpi) {
+    int pr[kEpi][16];
+    float gw[kEpi][16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = gemm_row(i, q);
-      if (row >= m) continue;
-      const int pair = p.rows[r0 + row];
-      const int tok = pair / p.nslot, s = pair - tok * p.nslot;
-      const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
-      float *dst = p.slots + static_cast<size_t>(pair) * d + n0;
+    for (int i = 0; i < kEpi; ++i)
 #pragma unroll
-      for (int j = 0; j < kGWaveN / 32; ++j) dst[gemm_col(j)] = w * acc[i][j][q];
-    }
+      for (int q = 0; q < 16; ++q) pr[i][q] = p.rows[r0 + min(gemm_row(i0 + i, q), m - 1)];
+#pragma unroll
+    for (int i = 0; i < kEpi; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int tok = pr[i][q] / p.nslot, s = pr[i][q] - tok * p.nslot;
+        gw[i][q] = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
+      }
+#pragma unroll
+    for (int i = 0; i < kEpi; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = gemm_row(i0 + i, q);
+        if (row >= m) continue;
+        const int pair = pr[i][q];
+        const float w = gw[i][q];
+        float *dst = p.slots + static_cast<size_t>(pair) * d + n0;
+#pragma unroll
+        for (int j = 0; j < kGWaveN / 32; ++j) dst[gemm_col(j)] = w * acc[i0 + i][j][q];
+      }
+  }
 }
 
 // Shared experts' down projection over every token, with the combine in
 // the epilogue: K runs over the S shared experts laid end to end (their a
 // rows and W_down columns), y = ((slot_0 + ... + slot_{k-1}) + shared) in
-// that order, h_dst = round(h_src + y).  Row tiles of kGBM tokens.
-template <int NK>
+// that order, h_dst = round(h_src + y).  Row tiles of kGBM tokens.  KT > 0
+// fixes top_k at compile time (0: p.k, up to kMaxTopK).
+template <int NK, int KT>
 __global__ __launch_bounds__(kGThreads) void k_gemm_down_shared(ExpertArgs p, CombineArgs c) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   GemmSmem &sm = *reinterpret_cast<GemmSmem *>(smem_raw);
@@ -347,38 +370,69 @@ __global__ __launch_bounds__(kGThreads) void k_gemm_down_shared(ExpertArgs p, Co
       for (int qq = 0; qq < 16; ++qq) acc[i][j][qq] = 0.f;
   if (S > 0) gemm_mainloop<NK>(sm, A, B, S * F / kGBK, acc);
 
-  // epilogue: per row, the slot loads of all of this lane's columns are
-  // issued together (slot index clamped, surplus terms masked) before the
-  // sums, which keep the order slot 0, 1, ..., k-1, then the shared part
+  // Epilogue through LDS, in kGMT rounds: in round r every wavefront stages
+  // its 32-row MFMA tile r (block rows wm*64 + r*32 .. +31; 128 rows in all),
+  // then each wavefront takes whole staged rows, lane l columns 4l .. 4l+3,
+  // so the slot and residual loads and the stores run along rows in 16- and
+  // 8-byte pieces, kRowsInFlight rows per lane loaded before any is stored.
+  constexpr int NJ = kGWaveN / 32;
+  constexpr int kStLd = kGBN + 4;             // fp32 row stride of the staged rows
+  constexpr int kStaged = kGWavesM * 32;      // rows staged per round
+  constexpr int kWaves = kGThreads / kWave;
+  constexpr int kRowsInFlight = KT > 0 ? 4 : 2;  // up to kMaxTopK slot loads per row otherwise
+  constexpr int KS = KT > 0 ? KT : kMaxTopK;  // slot loads per row
+  static_assert(kStaged * kStLd * 4 <= static_cast<int>(sizeof(GemmSmem)), "staged rows fit the LDS");
+  static_assert(kGBN == 4 * kWave, "one lane per 4 columns");
+  const int k = KT > 0 ? KT : p.k;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv % kGWavesM;
+  float *stage = reinterpret_cast<float *>(smem_raw);
   const bf16_t *hs = static_cast<const bf16_t *>(c.h_src);
   bf16_t *hd = static_cast<bf16_t *>(c.h_dst);
-  constexpr int NJ = kGWaveN / 32;
 #pragma unroll
-  for (int i = 0; i < kGMT; ++i)
-#pragma unroll 4
-    for (int qq = 0; qq < 16; ++qq) {
-      const int t_raw = t0 + gemm_row(i, qq), t = min(t_raw, T - 1);
-      const float *sp = p.slots + static_cast<size_t>(t) * p.nslot * d + n0;
-      float v[kMaxTopK][NJ];
+  for (int r = 0; r < kGMT; ++r) {
+    __syncthreads();  // the K loop's last LDS reads, or the previous round's, are done
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s) {
-        const int ss = min(s, p.k - 1);
+    for (int qq = 0; qq < 16; ++qq)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) v[s][j] = sp[static_cast<size_t>(ss) * d + gemm_col(j)];
+      for (int j = 0; j < NJ; ++j)
+        stage[(wm * 32 + (qq >> 2) * 8 + (lane >> 5) * 4 + (qq & 3)) * kStLd + gemm_col(j)] = acc[r][j][qq];
+    __syncthreads();
+    for (int u0 = 0; u0 < kStaged / kWaves; u0 += kRowsInFlight) {
+      float4 sv[kRowsInFlight][KS];
+      uint2 hv[kRowsInFlight];
+      int tr[kRowsInFlight];
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        const int sr = wv + (u0 + u) * kWaves;  // staged row: block row (sr/32)*64 + r*32 + sr%32
+        tr[u] = t0 + (sr / 32) * kGWaveM + r * 32 + sr % 32;
+        const size_t t = static_cast<size_t>(min(tr[u], T - 1));
+        const float *sp = p.slots + t * p.nslot * d + n0 + lane * 4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          sv[u][s] = *reinterpret_cast<const float4 *>(sp + static_cast<size_t>(min(s, k - 1)) * d);
+        hv[u] = ld8(hs + t * d + n0 + lane * 4);
       }
-      if (t_raw >= T) continue;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        float y = 0.f;
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        if (tr[u] >= T) continue;
+        const int sr = wv + (u0 + u) * kWaves;
+        const float4 sh = *reinterpret_cast<const float4 *>(stage + sr * kStLd + lane * 4);
+        float y[4] = {0.f, 0.f, 0.f, 0.f}, hf[4], o[4];
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-          if (s < p.k) y += v[s][j];
-        y += acc[i][j][qq];
-        const size_t o = static_cast<size_t>(t) * d + n0 + gemm_col(j);
-        hd[o] = f32_to_bf16(to_f32(hs[o]) + y);
-        if (c.y_moe) c.y_moe[o] = y;
+        for (int s = 0; s < KS; ++s)
+          if (s < k) {
+            y[0] += sv[u][s].x; y[1] += sv[u][s].y; y[2] += sv[u][s].z; y[3] += sv[u][s].w;
+          }
+        y[0] += sh.x; y[1] += sh.y; y[2] += sh.z; y[3] += sh.w;
+        unpack8(hv[u], hf, bf16_t());
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = round_to<bf16_t>(hf[e] + y[e]);
+        const size_t off = static_cast<size_t>(tr[u]) * d + n0 + lane * 4;
+        st8(hd + off, pack8(o, bf16_t()));
+        if (c.y_moe) *reinterpret_cast<float4 *>(c.y_moe + off) = make_float4(y[0], y[1], y[2], y[3]);
       }
     }
+  }
 }
 
 }  // namespace
@@ -413,14 +467,14 @@ hipError_t launch_gemm_down(const ExpertArgs &a, int max_tiles, hipStream_t s) {
 hipError_t launch_gemm_down_shared(const ExpertArgs &a, const CombineArgs &c, hipStream_t s) {
   const int items = (a.T + kGBM - 1) / kGBM * (a.d / kGBN);
   const int grid = (items + kXcds - 1) / kXcds * kXcds;
-  const bool unrolled = a.S == 2 && a.F == kNkF * kGBK;
-  const void *k = unrolled ? reinterpret_cast<const void *>(k_gemm_down_shared<2 * kNkF>)
-                           : reinterpret_cast<const void *>(k_gemm_down_shared<0>);
+  const bool unrolled = a.S == 2 && a.F == kNkF * kGBK && a.k == 6;
+  const void *k = unrolled ? reinterpret_cast<const void *>(k_gemm_down_shared<2 * kNkF, 6>)
+                           : reinterpret_cast<const void *>(k_gemm_down_shared<0, 0>);
   (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(GemmSmem));
   if (unrolled)
-    hipLaunchKernelGGL(k_gemm_down_shared<2 * kNkF>, dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
+    hipLaunchKernelGGL((k_gemm_down_shared<2 * kNkF, 6>), dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
   else
-    hipLaunchKernelGGL(k_gemm_down_shared<0>, dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
+    hipLaunchKernelGGL((k_gemm_down_shared<0, 0>), dim3(grid), dim3(kGThreads), sizeof(GemmSmem), s, a, c);
   return hipGetLastError();
 }
 
