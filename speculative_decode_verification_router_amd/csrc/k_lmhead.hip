@@ -68,18 +68,22 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   const int r0 = blockIdx.y * kTileM;
   const int m = min(kTileM, p.T - r0);
   const int d = p.d, nvec = d / VN, lda = d + VN;
-  T *A = reinterpret_cast<T *>(smem);
+  T *A = reinterpret_cast<T *>(smem);  // rows [0, m) of x_f, then a zero row
   __shared__ unsigned long long red[kLmWaves][kTileM];
 
+  LmStream<T> ls;
+  ls.begin(p, blockIdx.x, threadIdx.x);  // weights requested before x_f is staged
   const T *xf = static_cast<const T *>(p.xf);
-  for (int i = threadIdx.x; i < kTileM * nvec; i += blockDim.x) {
+  for (int i = threadIdx.x; i < (m + 1) * nvec; i += blockDim.x) {
     const int r = i / nvec, c = i - r * nvec;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r < m) v = ld16(xf + static_cast<size_t>(r0 + r) * d + c * VN);
     st16(A + r * lda + c * VN, v);
   }
   __syncthreads();
-  lm_rows_block<T>(p, blockIdx.x, r0, m, A, lda, red, threadIdx.x);
+  const int lane = threadIdx.x & 63;
+  const int arow = (lane & 15) < m ? (lane & 15) : m;
+  ls.finish(p, r0, m, A + arow * lda + (lane >> 4) * VN, red, threadIdx.x);
   lm_block_done(p);
 }
 
@@ -242,7 +246,8 @@ hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s) {
   if (a.T > kTileM && slabs) return dtype == 1 ? launch_lm_rows<bf16_t>(a, s) : launch_lm_rows<float>(a, s);
   const int rows_per_block = 16 * kLmSlices * kLmWaves;
   const dim3 grid((a.V + rows_per_block - 1) / rows_per_block, (a.T + kTileM - 1) / kTileM);
-  const size_t smem = kTileM * (a.d + 16 / es) * es;
+  const size_t rows = (a.T < kTileM ? a.T : kTileM) + 1;  // the largest tile's rows and a zero row
+  const size_t smem = rows * (a.d + 16 / es) * es;
   if (smem > 65536) {
     const void *k = dtype == 1 ? reinterpret_cast<const void *>(k_lm_argmax<bf16_t>)
                                : reinterpret_cast<const void *>(k_lm_argmax<float>);

@@ -27,7 +27,7 @@ constexpr int kRLQuarterWin = 20;  // K windows per quarter held in registers (a
 constexpr int kScatterThreads = 256;
 
 struct RLSmem {
-  size_t x, p, lg, key, inv, sel, total;
+  size_t x, p, lg, key, inv, sel, g, total;
 };
 __host__ __device__ inline RLSmem rl_smem(int d) {
   const int nvec = d / 8;
@@ -38,7 +38,8 @@ __host__ __device__ inline RLSmem rl_smem(int d) {
   s.key = s.lg + static_cast<size_t>(4) * kRLTok * 64 * 4;         // [16][64] top-k keys
   s.inv = s.key + static_cast<size_t>(kRLTok) * 64 * 8;            // [16]
   s.sel = s.inv + kRLTok * 4;                                      // [16][kMaxTopK]
-  s.total = s.sel + kRLTok * kMaxTopK * 4;
+  s.g = s.sel + kRLTok * kMaxTopK * 4;                             // [d] gamma, bf16
+  s.total = s.g + static_cast<size_t>(d) * 2;
   return s;
 }
 
@@ -66,18 +67,26 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   uint4 b[kRLQuarterWin];
 #pragma unroll
   for (int u = 0; u < kRLQuarterWin; ++u) b[u] = ld16(wr + min(w_lo + u, w_hi - 1) * 16);
+  // gamma to LDS, requested with the rows (read by the x pass below, which
+  // also stores x_out: a global gamma load there would wait for those stores)
+  const bf16_t *gam = static_cast<const bf16_t *>(a.gamma);
+  bf16_t *gl = reinterpret_cast<bf16_t *>(smem + L.g);
+  uint4 gv = make_uint4(0, 0, 0, 0);
+  if (tid < nvec) gv = ld16(gam + tid * 8);
   // rows, chunk partial sums of squares; rows nt..16 are zero (row 16 feeds
-  // the MFMA tile's rows 16..31)
-  for (int it0 = tid; it0 < (kRLTok + 1) * nvec; it0 += 4 * kRLThreads) {
-    uint4 v[4];  // four loads in flight per thread
+  // the MFMA tile's rows 16..31).  kRowLoads loads per thread cover all
+  // 17 rows in one round trip for d <= 1280.
+  constexpr int kRowLoads = 6;
+  for (int it0 = tid; it0 < (kRLTok + 1) * nvec; it0 += kRowLoads * kRLThreads) {
+    uint4 v[kRowLoads];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRowLoads; ++u) {
       const int it = it0 + u * kRLThreads, r = it / nvec, ch = it - r * nvec;
       v[u] = make_uint4(0, 0, 0, 0);
       if (it < (kRLTok + 1) * nvec && r < nt) v[u] = ld16(h + static_cast<size_t>(t0 + r) * d + ch * 8);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRowLoads; ++u) {
       const int it = it0 + u * kRLThreads, r = it / nvec, ch = it - r * nvec;
       if (it >= (kRLTok + 1) * nvec) break;
       if (r < nt) {
@@ -91,6 +100,7 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
       st16(xl + r * ld + ch * 8, v[u]);
     }
   }
+  if (tid < nvec) st16(gl + tid * 8, gv);
   __syncthreads();
   for (int r = wv; r < nt; r += kRLThreads / kWave) {
     float acc = 0.f;
@@ -100,13 +110,12 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
     if (lane == 0) inv[r] = 1.0f / sqrtf(acc / static_cast<float>(d) + a.eps);
   }
   __syncthreads();
-  const bf16_t *gam = static_cast<const bf16_t *>(a.gamma);
   bf16_t *xo = static_cast<bf16_t *>(a.x_out);
   for (int it = tid; it < nt * nvec; it += blockDim.x) {
     const int r = it / nvec, ch = it - r * nvec;
     float hv[8], g[8], x[8];
     unpack(ld16(xl + r * ld + ch * 8), hv, bf16_t());
-    unpack(ld16(gam + ch * 8), g, bf16_t());
+    unpack(ld16(gl + ch * 8), g, bf16_t());
     const float s = inv[r];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = round_to<bf16_t>((hv[i] * s) * g[i]);
@@ -142,9 +151,7 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   __syncthreads();
   for (int r = wv; r < nt; r += kRLThreads / kWave)
     select_top_k(lg + r * 64, keys + r * 64, sel + r * kMaxTopK, a.E, a.k, a.ids + (t0 + r) * a.k,
-                 a.gates + (t0 + r) * a.k);
-  __syncthreads();
-  for (int i = tid; i < nt * a.k; i += blockDim.x) atomicAdd(&cnt[a.ids[t0 * a.k + i]], 1);
+                 a.gates + (t0 + r) * a.k, cnt);
   __syncthreads();
   if (tid < 64) blk_cnt[blockIdx.x * 64 + tid] = cnt[tid];
 }

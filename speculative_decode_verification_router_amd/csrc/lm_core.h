@@ -8,67 +8,97 @@ namespace mv {
 
 constexpr int kLmWaves = 4;
 constexpr int kLmSlices = 4;   // 16-row vocabulary slices per wavefront
-constexpr int kLmUnroll = 16;
+constexpr int kLmUnroll = 10;  // K-windows per weight batch; two batches in flight
 constexpr int kLmRowsPerBlock = 16 * kLmSlices * kLmWaves;
 
 // Vocabulary block `vblk` (kLmRowsPerBlock rows: kLmWaves wavefronts of
-// kLmSlices 16-row slices) of the LM head against up to 16 x_f rows staged
-// in LDS (A, row stride lda, rows >= m zero), by 256 threads with local
-// index tid: per row the best (value, ~id) key of the block is folded into
-// argkey[rbase + row] with one atomicMax (one block barrier inside).
+// kLmSlices 16-row slices) of the LM head against up to 16 x_f rows.  Each
+// wavefront streams its slices' weight rows as one sequence of batches of
+// kLmUnroll windows, the next batch requested before the current one is
+// multiplied; begin() requests the first batch, so a kernel can issue it
+// before it stages the x_f rows.
 template <typename T>
-__device__ __forceinline__ void lm_rows_block(const LmArgs &p, int vblk, int rbase, int m, const T *A, int lda,
-                                              unsigned long long (*red)[kTileM], int tid) {
-  constexpr int VN = Vec<T>::N, WIN = 4 * VN;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int koff = (lane >> 4) * VN;
-  const T *ar = A + (lane & 15) * lda + koff;
-  const int nwin = p.d / WIN;
-  uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
-  const int vbase = (vblk * kLmWaves + wv) * 16 * kLmSlices;
-  for (int sl = 0; sl < kLmSlices; ++sl) {
-    const int v0 = vbase + sl * 16;
-    if (v0 >= p.V) break;
-    const int v = v0 + (lane & 15);
-    const T *b = static_cast<const T *>(p.w) + static_cast<size_t>(min(v, p.V - 1)) * p.d + koff;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int w0 = 0; w0 < nwin; w0 += kLmUnroll) {
-      uint4 q[kLmUnroll];
+struct LmStream {
+  static constexpr int VN = Vec<T>::N, WIN = 4 * VN;
+  int vbase, nwin, bps, nb, koff;
+  uint4 qa[kLmUnroll], qb[kLmUnroll];
+
+  __device__ __forceinline__ const T *row(const LmArgs &p, int slice) const {
+    const int v = min(vbase + slice * 16 + static_cast<int>(threadIdx.x & 15), p.V - 1);
+    return static_cast<const T *>(p.w) + static_cast<size_t>(v) * p.d + koff;
+  }
+  // batch g: slice g / bps, windows from (g % bps) * kLmUnroll
+  __device__ __forceinline__ void load(const LmArgs &p, uint4 *q, int g) const {
+    const int slice = g / bps, w0 = (g - slice * bps) * kLmUnroll;
+    const T *b = row(p, slice);
 #pragma unroll
-      for (int u = 0; u < kLmUnroll; ++u)
-        if (w0 + u < nwin) q[u] = ld16(b + (w0 + u) * WIN);
+    for (int u = 0; u < kLmUnroll; ++u)
+      if (w0 + u < nwin) q[u] = ld16(b + (w0 + u) * WIN);
+  }
+  __device__ __forceinline__ void begin(const LmArgs &p, int vblk, int tid) {
+    const int lane = tid & 63, wv = tid >> 6;
+    koff = (lane >> 4) * VN;
+    nwin = p.d / WIN;
+    bps = (nwin + kLmUnroll - 1) / kLmUnroll;
+    nb = kLmSlices * bps;
+    vbase = (vblk * kLmWaves + wv) * 16 * kLmSlices;
+    load(p, qa, 0);
+  }
+  // MFMAs of batch g; after the last batch of a slice its logits are folded
+  // into the running (value, ~id) maximum of each of this lane's rows
+  __device__ __forceinline__ void step(const LmArgs &p, const uint4 *q, int g, const T *arow, f32x4_t &acc,
+                                       uint64_t *best) const {
+    const int slice = g / bps, w0 = (g - slice * bps) * kLmUnroll;
 #pragma unroll
-      for (int u = 0; u < kLmUnroll; ++u)
-        if (w0 + u < nwin) mfma16(acc, ld16(ar + (w0 + u) * WIN), q[u], T());
+    for (int u = 0; u < kLmUnroll; ++u)
+      if (w0 + u < nwin) mfma16(acc, ld16(arow + (w0 + u) * WIN), q[u], T());
+    if (w0 + kLmUnroll >= nwin) {
+      const int v = vbase + slice * 16 + static_cast<int>(threadIdx.x & 15);
+      if (v < p.V) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t key = argmax_key(acc[i], static_cast<uint32_t>(v));
+          best[i] = key > best[i] ? key : best[i];
+        }
+      }
+      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    if (v < p.V) {
+  }
+  // arow: this lane's x_f row in LDS (row (lane % 16), or a zero row past
+  // the m rows), at its K offset.  Per row the best key of the block is
+  // folded into argkey[rbase + row] with one atomicMax (one block barrier).
+  __device__ void finish(const LmArgs &p, int rbase, int m, const T *arow, unsigned long long (*red)[kTileM],
+                         int tid) {
+    const int lane = tid & 63, wv = tid >> 6;
+    uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < nb; g += 2) {
+      if (g + 1 < nb) load(p, qb, g + 1);
+      step(p, qa, g, arow, acc, best);
+      if (g + 2 < nb) load(p, qa, g + 2);
+      if (g + 1 < nb) step(p, qb, g + 1, arow, acc, best);
+    }
+    // maximum over the 16 lanes that share rows 4*(lane/16)..+3
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint64_t key = argmax_key(acc[i], static_cast<uint32_t>(v));
-        best[i] = key > best[i] ? key : best[i];
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const uint64_t other = shfl_xor_u64(best[i], o);
+        best[i] = other > best[i] ? other : best[i];
       }
     }
-  }
-  // maximum over the 16 lanes that share rows 4*(lane/16)..+3
+    if ((lane & 15) == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) red[wv][(lane >> 4) * 4 + i] = best[i];
+    }
+    __syncthreads();
+    if (tid < m) {
+      uint64_t k = 0ull;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const uint64_t other = shfl_xor_u64(best[i], o);
-      best[i] = other > best[i] ? other : best[i];
+      for (int w = 0; w < kLmWaves; ++w) k = red[w][tid] > k ? red[w][tid] : k;
+      if (k != 0ull) atomicMax(p.argkey + rbase + tid, static_cast<unsigned long long>(k));
     }
   }
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wv][(lane >> 4) * 4 + i] = best[i];
-  }
-  __syncthreads();
-  if (tid < m) {
-    uint64_t k = 0ull;
-#pragma unroll
-    for (int w = 0; w < kLmWaves; ++w) k = red[w][tid] > k ? red[w][tid] : k;
-    if (k != 0ull) atomicMax(p.argkey + rbase + tid, static_cast<unsigned long long>(k));
-  }
-}
+};
 
 }  // namespace mv

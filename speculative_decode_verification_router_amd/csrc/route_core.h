@@ -83,10 +83,11 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
 // real key) and every lane counts the keys above its own, two per read.
 // key_lds: 64 keys, 16-byte aligned; sel_lds: kMaxTopK floats.  kCoherent:
 // the logits were written by other blocks of the same launch and are read
-// with agent-scope loads.
+// with agent-scope loads.  cnt_lds (LDS, optional): 1 is added to the count
+// of every chosen expert.
 template <bool kCoherent = false>
 __device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_lds, float *sel_lds, int E,
-                                             int k, int *ids, float *gates) {
+                                             int k, int *ids, float *gates, int *cnt_lds = nullptr) {
   const int lane = threadIdx.x & 63;
   const float logit = kCoherent ? __hip_atomic_load(lg_row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                 : lg_row[lane];
@@ -110,6 +111,7 @@ __device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_
   if (chosen) {
     sel_lds[rank] = ex;
     ids[rank] = lane;
+    if (cnt_lds) atomicAdd(cnt_lds + lane, 1);  // pairs per expert, counted in LDS
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
