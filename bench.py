@@ -26,7 +26,7 @@ METRIC = "committed tokens/s (12-layer MoE verify, K=3) + % of HBM/MFMA roofline
 # HBM bytes per b1_k3 verify step measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
 # (scaled by a 1 GiB copy; profiles/verify_step_b1_k3_hbm_counters.txt) on the
 # kernel sources with this digest; reported only while the sources match.
-MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "9cc141ab0e8d8dd9", "bytes_per_step": 2.1837e9}}
+MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "1492f3144441c505", "bytes_per_step": 2.1842e9}}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -144,7 +144,7 @@ def _timed(run, stream, steps, warmup, torch):
 
 def _header(args, wl):
     return {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
+            "scaling": "weak", "vs_baseline": None, "dtype": wl.dims.dtype}
 
 
 def bench_verify(args, wl, W, bd, synth, torch):
