@@ -38,9 +38,18 @@ are rounded to fp32 (the precision the kernel holds them in) before the
 integer decisions taken on them (top-6, argmax), and the decision margins are
 measured on those fp32 values.  Everything else stays float64.
 
+The FastMTP draft block (mtp_block, mtp_draft) follows the same pages'
+FastMTP paragraph: one dense block whose parameters are shared by every
+draft position, fed by the decoder's last hidden state and the token that
+follows it, drafting through the decoder's own LM head.  Its inner layers are
+not on the pages; the plainest reading is used: RMSNorm of the hidden state
+and of the token's embedding, a linear projection of the two laid end to end
+back to d, a residual dense SwiGLU FFN behind an RMSNorm, and an RMSNorm
+before the LM head.
+
 Parity status: every function here is pinned by tests/test_oracle_pins.py
-(library special cases, closed forms, invariants, brute force, and the
-lossless greedy-equivalence property).
+and tests/test_mtp_pins.py (library special cases, closed forms, invariants,
+brute force, and the lossless greedy-equivalence property).
 """
 from __future__ import annotations
 
@@ -281,3 +290,53 @@ def verify_step(h_in: np.ndarray, drafts: np.ndarray, W, dims) -> Dict[str, obje
     n_acc, committed, n_committed = spec_accept(g, drafts)
     out.update(n_accepted=n_acc, committed=committed, n_committed=n_committed)
     return out
+
+
+# ---------------------------------------------------------------------------
+# FastMTP draft block
+# ---------------------------------------------------------------------------
+
+
+def mtp_block(h: np.ndarray, tokens: np.ndarray, M: Dict[str, np.ndarray], dims,
+              ftype=np.float64):
+    """One application of the draft block to rows h [B, d] (stored values)
+    with the tokens [B] that follow them.
+
+    u  = [ R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e) ]      (2d values)
+    h1 = R(u W_proj^T)
+    h2 = R(h1 + SwiGLU(R(RMSNorm(h1) * g_ffn)))
+    R() is the storage rounding.  Returns (h1, h2).
+    """
+    dt, eps = dims.dtype, dims.rms_eps
+    e = widen(np.asarray(M["embed"])[np.asarray(tokens, np.int64)], dt)
+    uh = store(rms_norm(h, widen(M["norm_h"], dt), eps, ftype), dt)
+    ue = store(rms_norm(e, widen(M["norm_e"], dt), eps, ftype), dt)
+    u = np.concatenate([uh, ue], axis=1)
+    h1 = store(np.asarray(u, ftype) @ np.asarray(widen(M["w_proj"], dt), ftype).T, dt)
+    x = store(rms_norm(h1, widen(M["norm_ffn"], dt), eps, ftype), dt)
+    y = swiglu_expert(x, widen(M["w_gate_up"], dt), widen(M["w_down"], dt), dt, ftype)
+    h2 = store(np.asarray(h1, ftype) + y, dt)
+    return h1, h2
+
+
+def mtp_draft(h_in: np.ndarray, tokens: np.ndarray, M: Dict[str, np.ndarray], W, dims,
+              K: int, ftype=np.float64) -> Dict[str, np.ndarray]:
+    """K draft tokens per sequence.  h_in [B, d]: the decoder's last hidden
+    state of each sequence (its stored values); tokens [B]: the token that
+    follows it (the last committed one).  Draft j is the greedy choice of the
+    decoder's LM head on the block's output after RMSNorm (scale norm_out);
+    the block is then applied again to its own output and that draft.
+    Returns drafts [B, K], the block's last hidden state h_out, and each
+    draft's argmax margin [B, K]."""
+    h = widen(h_in, dims.dtype)
+    t = np.asarray(tokens, np.int64)
+    drafts, margins = [], []
+    for _ in range(K):
+        _, h = mtp_block(h, t, M, dims, ftype)
+        r = lm_head_argmax(h, M["norm_out"], W["lm_head"], dims, ftype=ftype)
+        t = np.asarray(r["argmax"], np.int64)
+        drafts.append(t)
+        margins.append(r["margin"])
+    B = h.shape[0]
+    return dict(drafts=np.stack(drafts, 1) if K else np.zeros((B, 0), np.int64), h_out=h,
+                margin=np.stack(margins, 1) if K else np.zeros((B, 0)))

@@ -82,7 +82,7 @@ WORKLOADS: Dict[str, Workload] = {
 # stream keys, one per tensor kind
 _K_NORM, _K_ROUTER, _K_RBIAS, _K_GU, _K_DOWN = 1, 2, 3, 4, 5
 _K_SGU, _K_SDOWN, _K_FNORM, _K_LM, _K_HIDDEN = 6, 7, 8, 9, 10
-_K_DRAFT, _K_EMB, _K_PERM = 11, 12, 13
+_K_DRAFT, _K_EMB, _K_PERM, _K_MTP = 11, 12, 13, 14
 
 _THREADS = max(1, min(16, os.cpu_count() or 1))
 
@@ -242,3 +242,52 @@ def make_embedding(dims: ModelDims, seed: int = 0) -> np.ndarray:
     (the decoder's real embedding is outside the verified path)."""
     v = _rng(seed, _K_EMB).standard_normal((dims.vocab, dims.d_model), dtype=np.float32)
     return _store(v, dims.dtype)
+
+
+# ---------------------------------------------------------------------------
+# FastMTP draft block
+# ---------------------------------------------------------------------------
+
+
+def mtp_d_ff(dims: ModelDims) -> int:
+    """Width of the draft block's dense SwiGLU FFN: 2F, the width of the two
+    always-on shared experts together (the pages give no width)."""
+    return 2 * dims.d_ff
+
+
+def make_mtp_weights(dims: ModelDims, seed: int = 0, sigma: Optional[float] = None,
+                     gamma: str = "ones") -> Dict[str, np.ndarray]:
+    """Weights of the FastMTP draft block (one dense block whose parameters
+    are shared by every draft position; its LM head is the decoder's own).
+
+    Layout (row-major, [out, in] per matrix):
+      embed     [V, d]        token embeddings ~ N(0, 1)
+      norm_h    [d]           RMSNorm scale of the incoming hidden state
+      norm_e    [d]           RMSNorm scale of the token's embedding
+      w_proj    [d, 2d]       projection of [norm(h) ; norm(e)]
+      norm_ffn  [d]           RMSNorm scale before the dense FFN
+      w_gate_up [2Fm, d]      rows [0, Fm) gate, [Fm, 2Fm) up
+      w_down    [d, Fm]
+      norm_out  [d]           RMSNorm scale before the LM head
+    sigma: standard deviation of the matrices; None means 1/sqrt(fan_in).
+    """
+    d, dt, Fm = dims.d_model, dims.dtype, mtp_d_ff(dims)
+
+    def sd(fan_in):
+        return sigma if sigma is not None else 1.0 / np.sqrt(fan_in)
+
+    m: Dict[str, np.ndarray] = {"embed": make_embedding(dims, seed)}
+    for i, (name, shape, fan) in enumerate([("w_proj", (d, 2 * d), 2 * d),
+                                            ("w_gate_up", (2 * Fm, d), d),
+                                            ("w_down", (d, Fm), Fm)]):
+        m[name] = _alloc(shape, dt)
+        _normal_block(m[name], (), sd(fan), dt, (seed, _K_MTP, i))
+    for i, name in enumerate(["norm_h", "norm_e", "norm_ffn", "norm_out"]):
+        if gamma == "ones":
+            v = np.ones(d, np.float32)
+        elif gamma == "uniform":
+            v = _rng(seed, _K_MTP, 10 + i).uniform(0.5, 1.5, d).astype(np.float32)
+        else:
+            raise ValueError(gamma)
+        m[name] = _store(v, dt)
+    return m
