@@ -73,6 +73,8 @@ def main(argv=None):
     ap.add_argument("--loop", action="store_true",
                     help="run the decode loop (sequences until --loop-tokens committed each)")
     ap.add_argument("--loop-tokens", type=int, default=1085)
+    ap.add_argument("--draft", action="store_true",
+                    help="time the FastMTP draft block (mtp_draft) for the workload's B and K")
     ap.add_argument("--k-draft", type=int, default=None)
     ap.add_argument("--match-p", type=float, default=None)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -107,6 +109,8 @@ def main(argv=None):
     W = synth.workload_weights(wl, seed=args.seed)
     if wl.batch == 0:
         line = bench_stack(args, wl, W, bd, synth, torch)
+    elif args.draft:
+        line = bench_draft(args, wl, W, bd, synth, torch)
     elif args.loop:
         line = bench_loop(args, wl, W, bd, synth, torch)
     else:
@@ -371,6 +375,66 @@ def bench_loop(args, wl, W, bd, synth, torch):
                    "tokens_per_sequence": target, "verify_steps": steps, "rows_verified": rows,
                    "committed": int(committed), "committed_per_seq_step": round(per_seq_step, 4)},
         "roofline": None,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 4),
+    })
+    return line
+
+
+def draft_bytes(dims, d_ff_mtp, B, K):
+    """Algorithmic HBM bytes of one mtp_draft call: per draft position the
+    block's matrices (projection [d, 2d], gate/up [2Fm, d], down [d, Fm]),
+    the LM head, four norm vectors, and per sequence an embedding row and
+    the hidden rows in and out."""
+    es = 2 if dims.dtype == "bf16" else 4
+    d = dims.d_model
+    per_pos = (2 * d * d + 3 * d_ff_mtp * d + dims.vocab * d + 4 * d) * es
+    return K * (per_pos + B * 3 * d * es)
+
+
+def bench_draft(args, wl, W, bd, synth, torch):
+    """The FastMTP draft block: one mtp_draft call drafts K tokens for each of
+    B sequences (K applications of the block, each with an LM-head pass)."""
+    dims = wl.dims
+    B, K = wl.batch, (args.k_draft if args.k_draft is not None else wl.k_draft)
+    model = bd.DeviceModel(dims, W, max_tokens=B * (K + 1))
+    M = synth.make_mtp_weights(dims, seed=args.seed, sigma=wl.weight_sigma)
+    mtp = bd.DeviceMtp(dims, M, max_rows=B)
+    h_np = synth.make_hidden(dims, B, args.seed, wl.code)
+    tok_np = (np.arange(B, dtype=np.int32) * 7919 + 11) % dims.vocab
+    h, tok = bd.to_device(h_np), bd.to_device(tok_np.astype(np.int32))
+    out = bd.run_mtp_draft(model, mtp, h, tok, K)
+
+    def step(stream):
+        bd.mtp_draft(model.cfg, model.weights, mtp.weights, B, K, h, tok, out["drafts"], out["h_out"],
+                     mtp.ws, mtp.ws_bytes, stream)
+
+    stream = torch.cuda.current_stream()
+    ms, wall, t_enq = _timed(step, stream, args.steps, args.warmup, torch)
+    nbytes = draft_bytes(dims, mtp.d_ff, B, K)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+
+        t0 = time.perf_counter()
+        O.mtp_draft(h_np, tok_np, M, W, dims, K)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(B * K / dt, 3), "unit": "draft tokens/s", "cores": _cores(), "kind": "oracle",
+               "sample": f"one mtp_draft call ({B} sequences, K={K}; float64 numpy oracle)",
+               "s_per_call": round(dt, 3)}
+    line = {"metric": "draft tokens/s (FastMTP draft block) + % of HBM roofline",
+            "value": round(B * K / (ms * 1e-3), 1), "unit": "draft tokens/s"}
+    line.update(_header(args, wl))
+    line.update({
+        "ms_per_step": round(ms, 4),
+        "data": "synthetic (seeded; draft-block weights N(0,0.02), hidden N(0,1))",
+        "config": {"workload": wl.name + "_draft", "batch": B, "k_draft": K, "d_model": dims.d_model,
+                   "d_ff_draft": mtp.d_ff, "vocab": dims.vocab},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole mtp_draft call (K x [row norms, projection, FFN, LM head])",
+                     "algorithmic_bytes_per_step": int(nbytes)},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 4),
     })

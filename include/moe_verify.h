@@ -149,6 +149,59 @@ int spec_accept(int32_t B, int32_t K, const int32_t *argmax,
                 const int32_t *drafts, int32_t *n_accepted,
                 int32_t *committed, int32_t *n_committed, void *stream);
 
+/* FastMTP draft block (FastMTP paragraph of the ainewsfeed page: one dense
+ * block whose parameters are shared by every draft position, drafting
+ * through the decoder's own LM head).  The block's inner layers are not on
+ * the pages; this library uses the plainest reading.  Weights in the config
+ * dtype, [out, in] row-major:
+ *   embed     [V, d]      token embeddings
+ *   norm_h    [d]         RMSNorm scale of the incoming hidden state
+ *   norm_e    [d]         RMSNorm scale of the token's embedding
+ *   w_proj    [d, 2d]     projection of [norm(h) ; norm(e)]
+ *   norm_ffn  [d]         RMSNorm scale before the dense FFN
+ *   w_gate_up [2Fm, d]    rows [0, Fm) gate, [Fm, 2Fm) up
+ *   w_down    [d, Fm]
+ *   norm_out  [d]         RMSNorm scale before the LM head
+ *   d_ff      Fm: a positive multiple of 64 */
+typedef struct {
+  const void *embed;
+  const void *norm_h;
+  const void *norm_e;
+  const void *w_proj;
+  const void *norm_ffn;
+  const void *w_gate_up;
+  const void *w_down;
+  const void *norm_out;
+  int32_t d_ff;
+} mtp_weights;
+
+/* Bytes of device workspace mtp_draft needs for up to max_rows sequences
+ * (256-byte aligned pointer expected).  Host-only, pure; 0 for an invalid
+ * config, an unsupported width or max_rows outside [0, 65535]. */
+size_t mtp_workspace_bytes(const mv_config *cfg, int32_t d_ff_mtp, int32_t max_rows);
+
+/* K draft tokens for each of B sequences.  Per sequence, from its hidden
+ * state h (the decoder's last hidden state, before the final norm, as
+ * moe_verify_step's h_out returns it) and the token t that follows it:
+ *   u  = [ R(RMSNorm(h) * norm_h) ; R(RMSNorm(embed[t]) * norm_e) ]
+ *   h1 = R(u w_proj^T)
+ *   h2 = R(h1 + (R(SiLU(x Wg^T) * (x Wu^T))) w_down^T),  x = R(RMSNorm(h1) * norm_ffn)
+ *   draft = lowest id among the maximal z,  z = R(RMSNorm(h2) * norm_out) lm_head^T
+ * R() rounds to the config dtype; every sum is fp32.  The next draft applies
+ * the same block to (h2, draft).
+ *   w         decoder weights; only lm_head is read
+ *   h_in      [B, d]  config dtype
+ *   tokens    [B]     int32; an id outside [0, V) is clamped into it
+ *   drafts    [B, K]  int32
+ *   h_out     [B, d]  the block's last h2 (NULL to skip); may alias h_in
+ * Limits: 0 <= K <= 15, B <= 65535; the projection and the dense FFN stage
+ * 16 rows of width 2d and d_ff in LDS: 16 * (2d + 16/elem) * elem and
+ * 16 * (d_ff + 16/elem) * elem bytes must each be at most 160 KiB
+ * (d <= 2048 and d_ff <= 5112 in bf16).  K = 0 or B = 0 does nothing. */
+int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weights *m, int32_t B,
+              int32_t K, const void *h_in, const int32_t *tokens, int32_t *drafts,
+              void *h_out, void *ws, size_t ws_bytes, void *stream);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char *mv_last_error(void);
 

@@ -20,7 +20,7 @@ MV_F32, MV_BF16 = 0, 1
 MV_OK, MV_ERR_NULL, MV_ERR_SHAPE, MV_ERR_UNSUPPORTED, MV_ERR_WORKSPACE, MV_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("mv_workspace_bytes", "moe_layer_forward", "moe_verify_step", "spec_accept",
-            "mv_last_error")
+            "mtp_workspace_bytes", "mtp_draft", "mv_last_error")
 
 
 class MvConfig(ctypes.Structure):
@@ -35,6 +35,12 @@ class MvWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "ffn_norm", "router_w", "router_b", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
         "final_norm", "lm_head")]
+
+
+class MtpWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "embed", "norm_h", "norm_e", "w_proj", "norm_ffn", "w_gate_up", "w_down", "norm_out")] + [
+        ("d_ff", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -62,6 +68,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_step.restype = ctypes.c_int
     lib.spec_accept.argtypes = [I, I, P, P, P, P, P, P]
     lib.spec_accept.restype = ctypes.c_int
+    mwp = ctypes.POINTER(MtpWeights)
+    lib.mtp_workspace_bytes.argtypes = [cfgp, I, I]
+    lib.mtp_workspace_bytes.restype = SZ
+    lib.mtp_draft.argtypes = [cfgp, wp, mwp, I, I, P, P, P, P, P, SZ, P]
+    lib.mtp_draft.restype = ctypes.c_int
     lib.mv_last_error.argtypes = []
     lib.mv_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -135,6 +146,17 @@ def spec_accept(B: int, K: int, argmax, drafts, n_accepted, committed, n_committ
                               _ptr(committed), _ptr(n_committed), _stream(stream)))
 
 
+def mtp_workspace_bytes(cfg: MvConfig, d_ff: int, max_rows: int) -> int:
+    return int(load().mtp_workspace_bytes(ctypes.byref(cfg), int(d_ff), int(max_rows)))
+
+
+def mtp_draft(cfg: MvConfig, weights: MvWeights, mtp: MtpWeights, B: int, K: int, h_in, tokens,
+              drafts, h_out=None, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(load().mtp_draft(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(mtp), B, K,
+                            _ptr(h_in), _ptr(tokens), _ptr(drafts), _ptr(h_out), _ptr(ws),
+                            ws_bytes, _stream(stream)))
+
+
 # ---------------------------------------------------------------- device memory
 
 
@@ -168,6 +190,36 @@ class DeviceModel:
             np.asarray(bias, np.float32), self.ws.device)
         m.weights = MvWeights(*[_ptr(m.tensors.get(n)) for n, _ in MvWeights._fields_])
         return m
+
+
+class DeviceMtp:
+    """FastMTP draft-block weights in device memory, the C struct pointing at
+    them, and a workspace for up to ``max_rows`` sequences."""
+
+    def __init__(self, dims, mtp: Dict[str, np.ndarray], max_rows: int, device: str = "cuda"):
+        import torch
+
+        names = [n for n, _ in MtpWeights._fields_ if n != "d_ff"]
+        self.tensors = {n: to_device(mtp[n], device) for n in names}
+        self.d_ff = int(mtp["w_down"].shape[1])
+        self.weights = MtpWeights(*[_ptr(self.tensors[n]) for n in names], self.d_ff)
+        cfg = make_config(dims)
+        self.ws_bytes = mtp_workspace_bytes(cfg, self.d_ff, max_rows)
+        if self.ws_bytes == 0 and max_rows > 0:
+            raise MvError(MV_ERR_UNSUPPORTED, mv_last_error())
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+
+
+def run_mtp_draft(model: DeviceModel, mtp: DeviceMtp, h_in, tokens, K: int, stream=None):
+    """Allocate drafts [B, K] and h_out [B, d], enqueue one mtp_draft (no sync)."""
+    import torch
+
+    B = h_in.shape[0]
+    out = dict(drafts=torch.empty((B, K), dtype=torch.int32, device=h_in.device),
+               h_out=torch.empty_like(h_in))
+    mtp_draft(model.cfg, model.weights, mtp.weights, B, K, h_in, tokens, out["drafts"],
+              out["h_out"], mtp.ws, mtp.ws_bytes, stream)
+    return out
 
 
 def to_device(arr: np.ndarray, device: str = "cuda"):

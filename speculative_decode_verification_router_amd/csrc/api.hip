@@ -432,4 +432,146 @@ MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_
   return hip_status(mv::launch_accept(aa, static_cast<hipStream_t>(stream)));
 }
 
+// ------------------------------------------------------- FastMTP draft block
+
+namespace {
+
+struct MtpLayout {
+  size_t u, acc, h1, x, a, hcur, xo, argkey, tinfo, tstart, rows, total;
+};
+
+MtpLayout mtp_layout(const mv_config &c, int Fm, int B) {
+  const size_t es = c.dtype == MV_BF16 ? 2 : 4, d = static_cast<size_t>(c.d_model), b = static_cast<size_t>(B);
+  MtpLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.u = take(b * 2 * d * es);
+  L.acc = take(b * d * 4);
+  L.h1 = take(b * d * es);
+  L.x = take(b * d * es);
+  L.a = take(b * static_cast<size_t>(Fm) * es);
+  L.hcur = take(b * d * es);
+  L.xo = take(b * d * es);
+  L.argkey = take(b * 8);
+  L.tinfo = take((b + mv::kTileM - 1) / mv::kTileM * 16);
+  L.tstart = take(2 * 4);
+  L.rows = take(b * 4);
+  L.total = off;
+  return L;
+}
+
+// The projection and the dense FFN stage 16 rows of width 2d and Fm in LDS.
+int check_mtp(const mv_config *c, int Fm) {
+  if (Fm <= 0 || Fm % 64) return fail(MV_ERR_UNSUPPORTED, "the draft block's d_ff must be a positive multiple of 64");
+  const size_t es = c->dtype == MV_BF16 ? 2 : 4, vn = 16 / es, lds = 160 * 1024;
+  if (static_cast<size_t>(mv::kTileM) * (2 * static_cast<size_t>(c->d_model) + vn) * es > lds)
+    return fail(MV_ERR_UNSUPPORTED, "2*d_model is too wide for the draft block's projection tile");
+  if (static_cast<size_t>(mv::kTileM) * (static_cast<size_t>(Fm) + vn) * es > lds)
+    return fail(MV_ERR_UNSUPPORTED, "the draft block's d_ff is too wide for its FFN tile");
+  return MV_OK;
+}
+
+// One-expert arguments of the dense kernels: rows [0, B) in tiles of 16.
+mv::ExpertArgs dense_args(const mv_config &c, int B, int K_in, const void *a_in, const void *w, char *ws,
+                          const MtpLayout &L) {
+  mv::ExpertArgs e{};
+  e.T = B;
+  e.d = c.d_model;
+  e.F = K_in;
+  e.E = 1;
+  e.S = 0;
+  e.k = 0;
+  e.nslot = 1;
+  e.x = a_in;
+  e.a = a_in;
+  e.w_routed = w;
+  e.tile_start = reinterpret_cast<int *>(ws + L.tstart);
+  e.rows = reinterpret_cast<int *>(ws + L.rows);
+  e.tile_info = reinterpret_cast<int4 *>(ws + L.tinfo);
+  e.slots = reinterpret_cast<float *>(ws + L.acc);
+  return e;
+}
+
+}  // namespace
+
+MV_API size_t mtp_workspace_bytes(const mv_config *cfg, int32_t d_ff_mtp, int32_t max_rows) {
+  if (check_config(cfg) != MV_OK || check_mtp(cfg, d_ff_mtp) != MV_OK) return 0;
+  if (max_rows < 0 || max_rows > kMaxTokens) {
+    g_err = "max_rows must be in [0, 65535]";
+    return 0;
+  }
+  return mtp_layout(*cfg, d_ff_mtp, max_rows).total;
+}
+
+MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weights *m, int32_t B, int32_t K,
+                     const void *h_in, const int32_t *tokens, int32_t *drafts, void *h_out, void *ws,
+                     size_t ws_bytes, void *stream) {
+  g_err.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w || !m) return fail(MV_ERR_NULL, "weights are NULL");
+  if (B < 0 || K < 0) return fail(MV_ERR_SHAPE, "B and K must be >= 0");
+  if (K > kMaxK) return fail(MV_ERR_SHAPE, "K must be at most 15");
+  if (B > kMaxTokens) return fail(MV_ERR_SHAPE, "B must be at most 65535");
+  if ((rc = check_mtp(cfg, m->d_ff))) return rc;
+  if (B == 0 || K == 0) return MV_OK;
+  if (!w->lm_head || !m->embed || !m->norm_h || !m->norm_e || !m->w_proj || !m->norm_ffn || !m->w_gate_up ||
+      !m->w_down || !m->norm_out)
+    return fail(MV_ERR_NULL, "a draft-block or LM-head weight pointer is NULL");
+  if (!h_in || !tokens || !drafts) return fail(MV_ERR_NULL, "h_in, tokens and drafts are required");
+  if (!ws) return fail(MV_ERR_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const MtpLayout L = mtp_layout(*cfg, m->d_ff, B);
+  if (ws_bytes < L.total) return fail(MV_ERR_WORKSPACE, "workspace smaller than mtp_workspace_bytes(cfg, d_ff, B)");
+
+  char *base = static_cast<char *>(ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = cfg->dtype, d = cfg->d_model, ntiles = (B + mv::kTileM - 1) / mv::kTileM;
+  mv::MtpArgs a{};
+  a.B = B;
+  a.K = K;
+  a.d = d;
+  a.V = cfg->vocab;
+  a.eps = cfg->rms_eps;
+  a.tokens = tokens;
+  a.argkey = reinterpret_cast<unsigned long long *>(base + L.argkey);
+  a.drafts = drafts;
+  a.rows = reinterpret_cast<int *>(base + L.rows);
+  a.tile_start = reinterpret_cast<int *>(base + L.tstart);
+  a.tile_info = reinterpret_cast<int4 *>(base + L.tinfo);
+  a.h_in = h_in;
+  a.h_cur = base + L.hcur;
+  a.h_out = h_out;
+  a.embed = m->embed;
+  a.norm_h = m->norm_h;
+  a.norm_e = m->norm_e;
+  a.norm_ffn = m->norm_ffn;
+  a.norm_out = m->norm_out;
+  a.u = base + L.u;
+  a.acc = reinterpret_cast<float *>(base + L.acc);
+  a.h1 = base + L.h1;
+  a.x = base + L.x;
+  a.xo = base + L.xo;
+
+  const mv::ExpertArgs proj = dense_args(*cfg, B, 2 * d, base + L.u, m->w_proj, base, L);
+  mv::ExpertArgs gate_up = dense_args(*cfg, B, m->d_ff, base + L.x, m->w_gate_up, base, L);
+  gate_up.a_out = base + L.a;
+  const mv::ExpertArgs down = dense_args(*cfg, B, m->d_ff, base + L.a, m->w_down, base, L);
+  const mv::LmArgs la{B, d, cfg->vocab, base + L.xo, w->lm_head, a.argkey, nullptr, mv::AcceptArgs{}};
+  for (int step = 0; step < K; ++step) {
+    if ((rc = hip_status(mv::launch_mtp_in(dt, a, step, s))) || (rc = hip_status(mv::launch_down(dt, proj, ntiles, s))) ||
+        (rc = hip_status(mv::launch_mtp_mid(dt, a, s))) ||
+        (rc = hip_status(mv::launch_gate_up(dt, gate_up, ntiles, s))) ||
+        (rc = hip_status(mv::launch_down(dt, down, ntiles, s))) ||
+        (rc = hip_status(mv::launch_mtp_out(dt, a, step == K - 1, s))) ||
+        (rc = hip_status(mv::launch_lm_argmax(dt, la, s))))
+      return rc;
+  }
+  return hip_status(mv::launch_mtp_last(a, s));
+}
+
 MV_API const char *mv_last_error(void) { return g_err.c_str(); }

@@ -119,6 +119,34 @@ struct LmArgs {
   AcceptArgs accept;
 };
 
+// FastMTP draft block, per-row kernels (k_mtp.hip).  Buffers are [B, ...]
+// rows in the config dtype unless noted.
+constexpr int kMtpMaxD = 4096;
+struct MtpArgs {
+  int B, K, d, V;
+  float eps;
+  const int *tokens;             // [B] input tokens (step 0)
+  unsigned long long *argkey;    // [B] LM-head argmax keys
+  int *drafts;                   // [B, K]
+  int *rows;                     // [B] one-expert tile table of the dense kernels
+  int *tile_start;               // [2]
+  int4 *tile_info;               // [ceil(B / 16)]
+  const void *h_in;              // [B, d] step 0's hidden state
+  void *h_cur;                   // [B, d] the block's output, next step's input
+  void *h_out;                   // [B, d] or null: the last step's output
+  const void *embed;             // [V, d]
+  const void *norm_h, *norm_e, *norm_ffn, *norm_out;  // [d]
+  void *u;                       // [B, 2d] projection input
+  float *acc;                    // [B, d] fp32: projection output, then FFN output
+  void *h1;                      // [B, d] projected hidden state
+  void *x;                       // [B, d] FFN input
+  void *xo;                      // [B, d] LM-head input
+};
+hipError_t launch_mtp_in(int dtype, const MtpArgs &a, int step, hipStream_t s);
+hipError_t launch_mtp_mid(int dtype, const MtpArgs &a, hipStream_t s);
+hipError_t launch_mtp_out(int dtype, const MtpArgs &a, int last, hipStream_t s);
+hipError_t launch_mtp_last(const MtpArgs &a, hipStream_t s);
+
 // dtype-dispatched launchers (dtype: 0 fp32, 1 bf16); return the launch error.
 hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int ntok, hipStream_t s);
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s);

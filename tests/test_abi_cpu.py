@@ -129,3 +129,63 @@ def test_spec_accept_rejects_bad_arguments(lib):
     assert lib.spec_accept(1, 3, None, FAKE, FAKE, FAKE, FAKE, None) == bd.MV_ERR_NULL
     assert lib.spec_accept(1, 3, FAKE, None, FAKE, FAKE, FAKE, None) == bd.MV_ERR_NULL
     assert lib.spec_accept(0, 3, None, None, None, None, None, None) == bd.MV_OK
+
+
+# ---------------------------------------------------------------- draft block
+
+
+def test_mtp_workspace_bytes(lib):
+    c = _cfg()
+    w1, w16 = bd.mtp_workspace_bytes(c, 1792, 1), bd.mtp_workspace_bytes(c, 1792, 16)
+    assert 0 < w1 < w16 and w16 % 256 == 0
+    # projection input [B, 2d], fp32 accumulator [B, d], FFN products [B, Fm]
+    assert w16 >= 16 * (2 * 1280 * 2 + 1280 * 4 + 1792 * 2)
+    assert bd.mtp_workspace_bytes(c, 1800, 4) == 0           # not a multiple of 64
+    assert bd.mtp_workspace_bytes(c, 8192, 4) == 0           # FFN tile too wide for LDS
+    assert bd.mtp_workspace_bytes(_cfg(d_model=4096), 1792, 4) == 0  # projection tile too wide
+    assert bd.mtp_workspace_bytes(c, 1792, -1) == 0
+    assert bd.mtp_workspace_bytes(_cfg(dims=synth.TINY_F32), 256, 4) > 0
+
+
+def _mtp(**kw):
+    m = bd.MtpWeights(*([FAKE] * 8), 1792)
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+def _draft(lib, cfg, w, m, B=1, K=3, h_in=FAKE, tokens=FAKE, drafts=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.mtp_draft(ctypes.byref(cfg), ctypes.byref(w) if w is not None else None,
+                         ctypes.byref(m) if m is not None else None, B, K, h_in, tokens, drafts,
+                         None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(w=None), bd.MV_ERR_NULL),
+    (dict(m=None), bd.MV_ERR_NULL),
+    (dict(h_in=None), bd.MV_ERR_NULL),
+    (dict(tokens=None), bd.MV_ERR_NULL),
+    (dict(drafts=None), bd.MV_ERR_NULL),
+    (dict(ws=None), bd.MV_ERR_NULL),
+    (dict(B=-1), bd.MV_ERR_SHAPE),
+    (dict(K=16), bd.MV_ERR_SHAPE),
+    (dict(B=70000), bd.MV_ERR_SHAPE),
+    (dict(ws_bytes=1024), bd.MV_ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), bd.MV_ERR_WORKSPACE),
+    (dict(m_kw=dict(d_ff=100)), bd.MV_ERR_UNSUPPORTED),
+    (dict(m_kw=dict(w_proj=None)), bd.MV_ERR_NULL),
+    (dict(w_kw=dict(lm_head=None)), bd.MV_ERR_NULL),
+])
+def test_mtp_draft_rejects_bad_arguments(lib, case, code):
+    case = dict(case)
+    w = _weights(**case.pop("w_kw", {})) if "w" not in case else case.pop("w")
+    m = _mtp(**case.pop("m_kw", {})) if "m" not in case else case.pop("m")
+    assert _draft(lib, _cfg(), w, m, **case) == code
+    assert bd.mv_last_error() != ""
+
+
+def test_mtp_draft_zero_work_is_a_no_op(lib):
+    assert _draft(lib, _cfg(), _weights(), _mtp(), B=0, h_in=None, tokens=None, drafts=None,
+                  ws=None) == bd.MV_OK
+    assert _draft(lib, _cfg(), _weights(), _mtp(), K=0, h_in=None, tokens=None, drafts=None,
+                  ws=None) == bd.MV_OK
