@@ -563,10 +563,11 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
   const mv::ExpertArgs down = dense_args(*cfg, B, m->d_ff, base + L.a, m->w_down, base, L);
   const mv::LmArgs la{B, d, cfg->vocab, base + L.xo, w->lm_head, a.argkey, nullptr, mv::AcceptArgs{}};
   for (int step = 0; step < K; ++step) {
-    if ((rc = hip_status(mv::launch_mtp_in(dt, a, step, s))) || (rc = hip_status(mv::launch_down(dt, proj, ntiles, s))) ||
+    if ((rc = hip_status(mv::launch_mtp_in(dt, a, step, s))) ||
+        (rc = hip_status(mv::launch_dense_down(dt, proj, ntiles, s))) ||
         (rc = hip_status(mv::launch_mtp_mid(dt, a, s))) ||
-        (rc = hip_status(mv::launch_gate_up(dt, gate_up, ntiles, s))) ||
-        (rc = hip_status(mv::launch_down(dt, down, ntiles, s))) ||
+        (rc = hip_status(mv::launch_dense_gate_up(dt, gate_up, ntiles, s))) ||
+        (rc = hip_status(mv::launch_dense_down(dt, down, ntiles, s))) ||
         (rc = hip_status(mv::launch_mtp_out(dt, a, step == K - 1, s))) ||
         (rc = hip_status(mv::launch_lm_argmax(dt, la, s))))
       return rc;

@@ -136,7 +136,9 @@ __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo 
   return true;
 }
 
-template <typename T>
+// U: K-windows per weight batch (kUnroll; the draft block's small grids use
+// kUnrollFused to keep more bytes in flight per block).
+template <typename T, int U = kUnroll>
 __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SmallTiles st;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   if (small ? !small_tile<kIdLoads>(p, p.ids, blockIdx.y, ti, st, first && threadIdx.x < kWave)
             : !table_tile(p, blockIdx.y, ti))
     return;
-  GateUpPart<T> part;
+  GateUpPart<T, U> part;
   part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while x is staged
 
   const int d = p.d, nvec = d / VN, lda = d + VN;
@@ -172,14 +174,14 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   part.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, up_acc, threadIdx.x);
 }
 
-template <typename T>
+template <typename T, int U = kUnroll>
 __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float half_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
   TileInfo ti;
   if (!table_tile(p, blockIdx.y, ti)) return;
-  DownPart<T> part;
+  DownPart<T, U> part;
   part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while a is staged
   stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
   __syncthreads();
@@ -461,20 +463,52 @@ void allow_lds(KernelT kernel, size_t bytes) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-}  // namespace
-
-hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+template <int U>
+hipError_t launch_gate_up_u(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
   const dim3 grid((a.F + 31) / 32, max_tiles);
   const size_t es = dtype == 1 ? 2 : 4;
   const size_t smem = kTileM * (a.d + 16 / es) * es;
   if (dtype == 1) {
-    allow_lds(k_gate_up<bf16_t>, smem);
-    hipLaunchKernelGGL(k_gate_up<bf16_t>, grid, dim3(kThreads), smem, s, a);
+    allow_lds(k_gate_up<bf16_t, U>, smem);
+    hipLaunchKernelGGL((k_gate_up<bf16_t, U>), grid, dim3(kThreads), smem, s, a);
   } else {
-    allow_lds(k_gate_up<float>, smem);
-    hipLaunchKernelGGL(k_gate_up<float>, grid, dim3(kThreads), smem, s, a);
+    allow_lds(k_gate_up<float, U>, smem);
+    hipLaunchKernelGGL((k_gate_up<float, U>), grid, dim3(kThreads), smem, s, a);
   }
   return hipGetLastError();
+}
+
+template <int U>
+hipError_t launch_down_u(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  const dim3 grid((a.d + 31) / 32, max_tiles);
+  const size_t es = dtype == 1 ? 2 : 4;
+  const size_t smem = kTileM * (a.F + 16 / es) * es;
+  if (dtype == 1) {
+    allow_lds(k_down<bf16_t, U>, smem);
+    hipLaunchKernelGGL((k_down<bf16_t, U>), grid, dim3(kThreads), smem, s, a);
+  } else {
+    allow_lds(k_down<float, U>, smem);
+    hipLaunchKernelGGL((k_down<float, U>), grid, dim3(kThreads), smem, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  return launch_gate_up_u<kUnroll>(dtype, a, max_tiles, s);
+}
+
+hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  return launch_down_u<kUnroll>(dtype, a, max_tiles, s);
+}
+
+hipError_t launch_dense_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  return launch_gate_up_u<kUnrollFused>(dtype, a, max_tiles, s);
+}
+
+hipError_t launch_dense_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
+  return launch_down_u<kUnrollFused>(dtype, a, max_tiles, s);
 }
 
 hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra, const CombineArgs *ca, int max_tiles,
@@ -500,20 +534,6 @@ hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra,
   } else {
     allow_lds(k_ffn_small<float>, smem);
     hipLaunchKernelGGL(k_ffn_small<float>, grid, dim3(kThreads), smem, s, a, r0, c0, max_tiles, n_route);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  const dim3 grid((a.d + 31) / 32, max_tiles);
-  const size_t es = dtype == 1 ? 2 : 4;
-  const size_t smem = kTileM * (a.F + 16 / es) * es;
-  if (dtype == 1) {
-    allow_lds(k_down<bf16_t>, smem);
-    hipLaunchKernelGGL(k_down<bf16_t>, grid, dim3(kThreads), smem, s, a);
-  } else {
-    allow_lds(k_down<float>, smem);
-    hipLaunchKernelGGL(k_down<float>, grid, dim3(kThreads), smem, s, a);
   }
   return hipGetLastError();
 }

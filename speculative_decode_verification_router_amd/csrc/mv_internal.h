@@ -152,6 +152,10 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+// The same 16-row kernels with kUnrollFused windows per weight batch, for
+// grids too small to fill the chip (the draft block's dense layers).
+hipError_t launch_dense_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_dense_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 // ra / ca: also route this layer inside the launch (kLogits), or null.
 hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra, const CombineArgs *ca, int max_tiles,
                             hipStream_t s);
