@@ -75,6 +75,9 @@ def main(argv=None):
     ap.add_argument("--loop-tokens", type=int, default=1085)
     ap.add_argument("--draft", action="store_true",
                     help="time the FastMTP draft block (mtp_draft) for the workload's B and K")
+    ap.add_argument("--with-draft", action="store_true",
+                    help="decode loop: run the draft block in every step (its cost is timed; the "
+                         "committed tokens follow the synthetic drafts of the given p)")
     ap.add_argument("--k-draft", type=int, default=None)
     ap.add_argument("--match-p", type=float, default=None)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -305,7 +308,21 @@ def bench_loop(args, wl, W, bd, synth, torch):
                 n_committed=torch.empty(B0, dtype=torch.int32, device="cuda"))
     zero = torch.zeros((B0, max(K, 1)), dtype=torch.int32, device="cuda")
 
+    mtp = None
+    if args.with_draft and K > 0:
+        mtp = bd.DeviceMtp(dims, synth.make_mtp_weights(dims, seed=args.seed, sigma=wl.weight_sigma),
+                           max_rows=B0)
+        d_scratch = torch.empty((B0, K), dtype=torch.int32, device="cuda")
+        tok = torch.zeros(B0, dtype=torch.int32, device="cuda")
+        first_rows = torch.arange(B0, device="cuda") * (K + 1)
+
     def verify(h_in, h_out, drafts, B):
+        if mtp is not None:
+            # the draft block's work for this step, from each sequence's first row: its
+            # drafts are computed (and timed); the verify step takes the planned ones
+            hsel = h_in.index_select(0, first_rows[:B])
+            bd.mtp_draft(model.cfg, model.weights, mtp.weights, B, K, hsel, tok[:B], d_scratch[:B], None,
+                         mtp.ws, mtp.ws_bytes, None)
         bd.moe_verify_step(model.cfg, model.weights, B, K, h_in, drafts, h_out, outs["argmax"],
                            outs["n_accepted"], outs["committed"], outs["n_committed"], None,
                            model.ws, model.ws_bytes, None)
@@ -373,6 +390,7 @@ def bench_loop(args, wl, W, bd, synth, torch):
         "data": "synthetic (seeded; weights N(0,0.02), Zipf router bias, drafts = argmax w.p. p)",
         "config": {"workload": wl.name, "sequences": B0, "k_draft": K, "match_p": p,
                    "tokens_per_sequence": target, "verify_steps": steps, "rows_verified": rows,
+                   "draft_block_in_step": mtp is not None,
                    "committed": int(committed), "committed_per_seq_step": round(per_seq_step, 4)},
         "roofline": None,
         "cpu_baseline": cpu,
