@@ -23,10 +23,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "committed tokens/s (12-layer MoE verify, K=3) + % of HBM/MFMA roofline"
-# HBM bytes per b1_k3 verify step measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
-# (scaled by a 1 GiB copy; profiles/verify_step_b1_k3_hbm_counters.txt) on the
-# kernel sources with this digest; reported only while the sources match.
-MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "1492f3144441c505", "bytes_per_step": 2.1842e9}}
+# HBM bytes per b1_k3 verify step and per b1_k3 mtp_draft call, measured with
+# rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by a 1 GiB copy;
+# profiles/verify_step_b1_k3_hbm_counters.txt, profiles/mtp_draft_b1_k3_hbm_counters.txt)
+# on the kernel sources with this digest; reported only while the sources match.
+MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "c0aa9a892e97faed", "bytes_per_step": 2.1841e9},
+                    "b1_k3_draft": {"csrc_sha256_16": "c0aa9a892e97faed", "bytes_per_step": 1.0559e9}}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -431,6 +433,8 @@ def bench_draft(args, wl, W, bd, synth, torch):
     ms, wall, t_enq = _timed(step, stream, args.steps, args.warmup, torch)
     nbytes = draft_bytes(dims, mtp.d_ff, B, K)
     achieved = nbytes / (ms * 1e-3) / 1e9
+    meas = MEASURED_TRAFFIC.get(wl.name + "_draft") if K == wl.k_draft else None
+    traffic = meas["bytes_per_step"] if meas and meas["csrc_sha256_16"] == csrc_digest() else None
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
@@ -450,7 +454,7 @@ def bench_draft(args, wl, W, bd, synth, torch):
         "config": {"workload": wl.name + "_draft", "batch": B, "k_draft": K, "d_model": dims.d_model,
                    "d_ff_draft": mtp.d_ff, "vocab": dims.vocab},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "whole mtp_draft call (K x [row norms, projection, FFN, LM head])",
                      "algorithmic_bytes_per_step": int(nbytes)},
         "cpu_baseline": cpu,
