@@ -195,9 +195,9 @@ size_t mtp_workspace_bytes(const mv_config *cfg, int32_t d_ff_mtp, int32_t max_r
  *   drafts    [B, K]  int32
  *   h_out     [B, d]  the block's last h2 (NULL to skip); may alias h_in
  * Limits: 0 <= K <= 15, B <= 65535; the projection and the dense FFN stage
- * 16 rows of width 2d and d_ff in LDS: 16 * (2d + 16/elem) * elem and
- * 16 * (d_ff + 16/elem) * elem bytes must each be at most 160 KiB
- * (d <= 2048 and d_ff <= 5112 in bf16).  K = 0 or B = 0 does nothing. */
+ * 16 rows of width 2d and d_ff in LDS: d_model <= 2112 and d_ff <= 4800 in
+ * bf16, d_model <= 1024 and d_ff <= 2368 in fp32 (MV_ERR_UNSUPPORTED beyond).
+ * K = 0 or B = 0 does nothing. */
 int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weights *m, int32_t B,
               int32_t K, const void *h_in, const int32_t *tokens, int32_t *drafts,
               void *h_out, void *ws, size_t ws_bytes, void *stream);

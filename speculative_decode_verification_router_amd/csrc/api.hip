@@ -437,7 +437,7 @@ MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_
 namespace {
 
 struct MtpLayout {
-  size_t u, acc, h1, x, a, hcur, xo, argkey, tinfo, tstart, rows, total;
+  size_t acc, acc2, a, hcur, xo, argkey, u, x, total;
 };
 
 MtpLayout mtp_layout(const mv_config &c, int Fm, int B) {
@@ -449,35 +449,33 @@ MtpLayout mtp_layout(const mv_config &c, int Fm, int B) {
     off += align256(bytes);
     return at;
   };
-  L.u = take(b * 2 * d * es);
   L.acc = take(b * d * 4);
-  L.h1 = take(b * d * es);
-  L.x = take(b * d * es);
+  L.acc2 = take(b * d * 4);
   L.a = take(b * static_cast<size_t>(Fm) * es);
   L.hcur = take(b * d * es);
   L.xo = take(b * d * es);
-  L.argkey = take(b * 8);
-  L.tinfo = take((b + mv::kTileM - 1) / mv::kTileM * 16);
-  L.tstart = take(2 * 4);
-  L.rows = take(b * 4);
+  L.argkey = take(2 * b * 8);
+  L.u = take(b > static_cast<size_t>(mv::kMtpFusedMaxB) ? b * 2 * d * es : 0);
+  L.x = take(b > static_cast<size_t>(mv::kMtpFusedMaxB) ? b * d * es : 0);
   L.total = off;
   return L;
 }
 
-// The projection and the dense FFN stage 16 rows of width 2d and Fm in LDS.
+// The projection and the dense FFN stage 16 rows of width 2d and Fm (and the
+// rows' chunk sums) in LDS.
 int check_mtp(const mv_config *c, int Fm) {
   if (Fm <= 0 || Fm % 64) return fail(MV_ERR_UNSUPPORTED, "the draft block's d_ff must be a positive multiple of 64");
-  const size_t es = c->dtype == MV_BF16 ? 2 : 4, vn = 16 / es, lds = 160 * 1024;
-  if (static_cast<size_t>(mv::kTileM) * (2 * static_cast<size_t>(c->d_model) + vn) * es > lds)
+  const int es = c->dtype == MV_BF16 ? 2 : 4;
+  const size_t lds = 152 * 1024;  // dynamic LDS, leaving room for the kernels' static arrays
+  if (mv::mtp_proj_lds(c->d_model, es) > lds)
     return fail(MV_ERR_UNSUPPORTED, "2*d_model is too wide for the draft block's projection tile");
-  if (static_cast<size_t>(mv::kTileM) * (static_cast<size_t>(Fm) + vn) * es > lds)
+  if (mv::mtp_ffn_lds(c->d_model, Fm, es) > lds)
     return fail(MV_ERR_UNSUPPORTED, "the draft block's d_ff is too wide for its FFN tile");
   return MV_OK;
 }
 
-// One-expert arguments of the dense kernels: rows [0, B) in tiles of 16.
-mv::ExpertArgs dense_args(const mv_config &c, int B, int K_in, const void *a_in, const void *w, char *ws,
-                          const MtpLayout &L) {
+// One-expert arguments of the dense layers: rows [0, B) in tiles of 16.
+mv::ExpertArgs dense_args(const mv_config &c, int B, int K_in, const void *a_in, const void *w, float *out) {
   mv::ExpertArgs e{};
   e.T = B;
   e.d = c.d_model;
@@ -489,10 +487,7 @@ mv::ExpertArgs dense_args(const mv_config &c, int B, int K_in, const void *a_in,
   e.x = a_in;
   e.a = a_in;
   e.w_routed = w;
-  e.tile_start = reinterpret_cast<int *>(ws + L.tstart);
-  e.rows = reinterpret_cast<int *>(ws + L.rows);
-  e.tile_info = reinterpret_cast<int4 *>(ws + L.tinfo);
-  e.slots = reinterpret_cast<float *>(ws + L.acc);
+  e.slots = out;
   return e;
 }
 
@@ -530,7 +525,7 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
 
   char *base = static_cast<char *>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int dt = cfg->dtype, d = cfg->d_model, ntiles = (B + mv::kTileM - 1) / mv::kTileM;
+  const int dt = cfg->dtype, d = cfg->d_model;
   mv::MtpArgs a{};
   a.B = B;
   a.K = K;
@@ -540,9 +535,6 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
   a.tokens = tokens;
   a.argkey = reinterpret_cast<unsigned long long *>(base + L.argkey);
   a.drafts = drafts;
-  a.rows = reinterpret_cast<int *>(base + L.rows);
-  a.tile_start = reinterpret_cast<int *>(base + L.tstart);
-  a.tile_info = reinterpret_cast<int4 *>(base + L.tinfo);
   a.h_in = h_in;
   a.h_cur = base + L.hcur;
   a.h_out = h_out;
@@ -551,24 +543,21 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
   a.norm_e = m->norm_e;
   a.norm_ffn = m->norm_ffn;
   a.norm_out = m->norm_out;
-  a.u = base + L.u;
   a.acc = reinterpret_cast<float *>(base + L.acc);
-  a.h1 = base + L.h1;
-  a.x = base + L.x;
+  a.acc2 = reinterpret_cast<float *>(base + L.acc2);
   a.xo = base + L.xo;
+  a.u = base + L.u;
+  a.x = base + L.x;
 
-  const mv::ExpertArgs proj = dense_args(*cfg, B, 2 * d, base + L.u, m->w_proj, base, L);
-  mv::ExpertArgs gate_up = dense_args(*cfg, B, m->d_ff, base + L.x, m->w_gate_up, base, L);
+  const mv::ExpertArgs proj = dense_args(*cfg, B, 2 * d, nullptr, m->w_proj, a.acc);
+  mv::ExpertArgs gate_up = dense_args(*cfg, B, m->d_ff, nullptr, m->w_gate_up, nullptr);
   gate_up.a_out = base + L.a;
-  const mv::ExpertArgs down = dense_args(*cfg, B, m->d_ff, base + L.a, m->w_down, base, L);
-  const mv::LmArgs la{B, d, cfg->vocab, base + L.xo, w->lm_head, a.argkey, nullptr, mv::AcceptArgs{}};
+  const mv::ExpertArgs down = dense_args(*cfg, B, m->d_ff, base + L.a, m->w_down, a.acc2);
   for (int step = 0; step < K; ++step) {
-    if ((rc = hip_status(mv::launch_mtp_in(dt, a, step, s))) ||
-        (rc = hip_status(mv::launch_dense_down(dt, proj, ntiles, s))) ||
-        (rc = hip_status(mv::launch_mtp_mid(dt, a, s))) ||
-        (rc = hip_status(mv::launch_dense_gate_up(dt, gate_up, ntiles, s))) ||
-        (rc = hip_status(mv::launch_dense_down(dt, down, ntiles, s))) ||
-        (rc = hip_status(mv::launch_mtp_out(dt, a, step == K - 1, s))) ||
+    // this position's LM head folds into key buffer step % 2
+    const mv::LmArgs la{B, d, cfg->vocab, a.xo, w->lm_head, a.argkey + static_cast<size_t>(step & 1) * B, nullptr,
+                        mv::AcceptArgs{}};
+    if ((rc = hip_status(mv::launch_mtp_position(dt, proj, gate_up, down, a, step, s))) ||
         (rc = hip_status(mv::launch_lm_argmax(dt, la, s))))
       return rc;
   }

@@ -136,8 +136,7 @@ __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo 
   return true;
 }
 
-// U: K-windows per weight batch (kUnroll; the draft block's small grids use
-// kUnrollFused to keep more bytes in flight per block).
+// U: K-windows per weight batch.
 template <typename T, int U = kUnroll>
 __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -501,14 +500,6 @@ hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStre
 
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
   return launch_down_u<kUnroll>(dtype, a, max_tiles, s);
-}
-
-hipError_t launch_dense_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  return launch_gate_up_u<kUnrollFused>(dtype, a, max_tiles, s);
-}
-
-hipError_t launch_dense_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  return launch_down_u<kUnrollFused>(dtype, a, max_tiles, s);
 }
 
 hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra, const CombineArgs *ca, int max_tiles,

@@ -1,70 +1,223 @@
-// Row kernels of the FastMTP draft block: one dense block whose parameters
-// are shared by every draft position, fed by the decoder's last hidden state
-// and the token that follows it, drafting through the decoder's own LM head
+// Kernels of the FastMTP draft block: one dense block whose parameters are
+// shared by every draft position, fed by the decoder's last hidden state and
+// the token that follows it, drafting through the decoder's own LM head
 // (FastMTP paragraph of "Jina AI Releases jina-ocr-v1, a 3.4B MoE Document
-// Parser With Built-In Speculative Decoding", ainewsfeed.tech).  The
-// projection and the dense SwiGLU FFN run on the 16-row expert-tile kernels
-// (k_gate_up, k_down) with a one-expert tile table; the LM head is the
-// verify step's.  These kernels do the per-row work in between, one block of
-// 256 threads per sequence:
+// Parser With Built-In Speculative Decoding", ainewsfeed.tech).  One draft
+// position is five launches:
 //
-//   k_mtp_in    token (the input token, or the previous draft from the LM
-//               head's argmax key, which it also records and clears),
-//               u = [R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e)]
-//   k_mtp_mid   h1 = R(z), x = R(RMSNorm(h1) * g_ffn)       (z = u W_proj^T)
-//   k_mtp_out   h2 = R(h1 + y), x_o = R(RMSNorm(h2) * g_out) (y = FFN(x))
-//   k_mtp_last  the last draft from the LM head's argmax key
+//   k_mtp_proj    z = u W_proj^T on 16-row tiles; each block builds the tile's
+//                 u = [R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e)] in LDS
+//                 itself (t: the input token, or the previous draft read from
+//                 the LM head's argmax key), and block (0, 0) records the
+//                 previous draft and clears the key buffer this step's LM
+//                 head will fold into
+//   k_mtp_ffn_gu  a = R(SiLU(x Wg^T) * (x Wu^T)), x = R(RMSNorm(R(z)) * g_ffn)
+//                 built in LDS by each block
+//   k_mtp_ffn_dn  y = a W_down^T
+//   k_mtp_out     h2 = R(R(z) + y) (the next position's h), x_o = R(RMSNorm(h2) * g_out)
+//   (LM head)     the verify step's k_lm_argmax on x_o
 //
-// The sum of squares of a row is taken per 16-byte chunk in order, then over
-// the chunks as in the verify step's RMSNorm.
-#include "mv_common.h"
-#include "mv_internal.h"
+// and k_mtp_last reads the last draft.  Above kMtpFusedMaxB sequences the
+// norms run in row kernels instead (k_mtp_in, k_mtp_mid; see below).  The
+// argmax keys alternate between two
+// buffers by position parity, so a projection reads the previous position's
+// keys while its block (0, 0) clears the other buffer.  The weight streams are
+// the expert-tile parts of expert_core.h with kUnrollFused windows per batch
+// (these grids are small).  A row's sum of squares is taken per 16-byte chunk
+// in order, then over the chunks as in the verify step's RMSNorm.
+#include "expert_core.h"
 
 namespace mv {
 
 namespace {
 
 constexpr int kRowThreads = 256;
+constexpr int kDenseU = kUnrollFused;
 
-// 1/rms of a row of d values produced by `val(chunk, out)` (VN values per
-// chunk), computed by the whole block; `part` is LDS of d / VN floats.
+// Chunks each thread loads before it uses any of them.
+constexpr int kChunksInFlight = 8;
+
+// 1/rms of rows [0, m) of a tile, rows given by val(row, chunk, out[VN]),
+// into inv[row]; part: LDS of m * d / VN floats.  Synchronises the block.
 template <int VN, typename F>
-__device__ __forceinline__ float block_inv_rms(int d, float eps, float *part, float *inv, F val) {
-  const int nvec = d / VN, tid = threadIdx.x, lane = tid & 63;
-  for (int ch = tid; ch < nvec; ch += blockDim.x) {
-    float v[VN];
-    val(ch, v);
-    float s = 0.f;
+__device__ __forceinline__ void tile_inv_rms(int m, int d, float eps, float *part, float *inv, F val) {
+  const int nvec = d / VN, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int it0 = tid; it0 < m * nvec; it0 += kChunksInFlight * blockDim.x) {
+    float v[kChunksInFlight][VN];
 #pragma unroll
-    for (int i = 0; i < VN; ++i) s += v[i] * v[i];
-    part[ch] = s;
+    for (int u = 0; u < kChunksInFlight; ++u) {
+      const int it = it0 + u * static_cast<int>(blockDim.x), r = it / nvec;
+      if (it < m * nvec) val(r, it - r * nvec, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kChunksInFlight; ++u) {
+      const int it = it0 + u * static_cast<int>(blockDim.x);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < VN; ++i) s += v[u][i] * v[u][i];
+      if (it < m * nvec) part[it] = s;
+    }
   }
   __syncthreads();
-  if (tid < kWave) {
+  for (int r = w; r < m; r += blockDim.x / kWave) {
     float acc = 0.f;
-    for (int ch = lane; ch < nvec; ch += kWave) acc += part[ch];
+    for (int ch = lane; ch < nvec; ch += kWave) acc += part[r * nvec + ch];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (lane == 0) *inv = 1.0f / sqrtf(acc / static_cast<float>(d) + eps);
+    if (lane == 0) inv[r] = 1.0f / sqrtf(acc / static_cast<float>(d) + eps);
   }
   __syncthreads();
-  return *inv;
 }
 
-// dst[0..d) = R((v * inv) * gamma), v from `val`.
-template <typename T, typename F>
-__device__ __forceinline__ void store_normed(int d, float inv, const T *gamma, T *dst, F val) {
+// VN fp32 values at p (16-byte aligned).
+template <int VN>
+__device__ __forceinline__ void ld_vec(const float *p, float *v) {
+  ld_f32<4>(p, v);
+  if constexpr (VN == 8) ld_f32<4>(p + 4, v + 4);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_mtp_proj(ExpertArgs p, MtpArgs a, int step) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float inv[2][kTileM];
+  __shared__ int tok[kTileM], rows[kTileM];
+  __shared__ float half_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
-  for (int ch = threadIdx.x; ch < d / VN; ch += blockDim.x) {
-    float v[VN], g[VN], o[VN];
-    val(ch, v);
-    unpack(ld16(gamma + ch * VN), g, T());
-#pragma unroll
-    for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[i] * inv) * g[i]);
-    st16(dst + ch * VN, pack(o, T()));
+  const int d = a.d, nvec = d / VN, lda = 2 * d + VN, tid = threadIdx.x, lane = tid & 63;
+  const int r0 = blockIdx.y * kTileM, m = min(kTileM, a.B - r0);
+  T *A = reinterpret_cast<T *>(smem);
+  float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(kTileM) * lda * sizeof(T));
+  const TileInfo ti{0, r0, m};
+  DownPart<T, kDenseU> part_w;
+  part_w.begin(p, ti, blockIdx.x, tid);  // weights in flight while u is built
+
+  const unsigned long long *key_prev = a.argkey + static_cast<size_t>((step - 1) & 1) * a.B;
+  if (tid < kTileM) {
+    rows[tid] = r0 + tid;
+    if (tid < m) {
+      const int b = r0 + tid;
+      const int t = step == 0 ? a.tokens[b] : static_cast<int>(key_index(key_prev[b]));
+      tok[tid] = min(max(t, 0), a.V - 1);
+    }
   }
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    unsigned long long *key_cur = a.argkey + static_cast<size_t>(step & 1) * a.B;
+    for (int b = tid; b < a.B; b += blockDim.x) {
+      if (step > 0) a.drafts[static_cast<size_t>(b) * a.K + step - 1] = static_cast<int>(key_index(key_prev[b]));
+      key_cur[b] = 0ull;
+    }
+  }
+  __syncthreads();
+  const T *h = static_cast<const T *>(step == 0 ? a.h_in : a.h_cur);
+  const T *emb = static_cast<const T *>(a.embed);
+  auto hv = [&](int r, int ch, float *v) { unpack(ld16(h + static_cast<size_t>(r0 + r) * d + ch * VN), v, T()); };
+  auto ev = [&](int r, int ch, float *v) { unpack(ld16(emb + static_cast<size_t>(tok[r]) * d + ch * VN), v, T()); };
+  tile_inv_rms<VN>(m, d, a.eps, part, inv[0], hv);
+  tile_inv_rms<VN>(m, d, a.eps, part, inv[1], ev);
+  // u = [R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e)] for rows [0, m) only: an
+  // MFMA output row depends on its own A row alone
+  const T *gh = static_cast<const T *>(a.norm_h), *ge = static_cast<const T *>(a.norm_e);
+  const int nu = m * 2 * nvec;
+  for (int it0 = tid; it0 < nu; it0 += kChunksInFlight * blockDim.x) {
+    float v[kChunksInFlight][VN];
+    uint4 gq[kChunksInFlight];
+#pragma unroll
+    for (int u = 0; u < kChunksInFlight; ++u) {
+      const int it = it0 + u * static_cast<int>(blockDim.x), r = it / (2 * nvec), c = it - r * 2 * nvec;
+      const int half = c >= nvec, ch = c - half * nvec;
+      if (it < nu) {
+        if (half) ev(r, ch, v[u]); else hv(r, ch, v[u]);
+        gq[u] = ld16((half ? ge : gh) + ch * VN);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunksInFlight; ++u) {
+      const int it = it0 + u * static_cast<int>(blockDim.x), r = it / (2 * nvec), c = it - r * 2 * nvec;
+      if (it >= nu) break;
+      float g[VN], o[VN];
+      unpack(gq[u], g, T());
+      const float sc = inv[c >= nvec][r];
+#pragma unroll
+      for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[u][i] * sc) * g[i]);
+      st16(A + r * lda + c * VN, pack(o, T()));
+    }
+  }
+  __syncthreads();
+  part_w.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, half_acc, tid, rows, nullptr);
 }
 
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_gu(ExpertArgs p, MtpArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float inv[kTileM];
+  __shared__ float up_acc[2][64][4];
+  constexpr int VN = Vec<T>::N;
+  const int d = a.d, nvec = d / VN, lda = d + VN, tid = threadIdx.x, lane = tid & 63;
+  const int r0 = blockIdx.y * kTileM, m = min(kTileM, a.B - r0);
+  T *A = reinterpret_cast<T *>(smem);
+  float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(kTileM) * lda * sizeof(T));
+  const TileInfo ti{0, r0, m};
+  GateUpPart<T, kDenseU> part_w;
+  part_w.begin(p, ti, blockIdx.x, tid);
+  auto h1v = [&](int r, int ch, float *v) {  // h1 = R(z)
+    ld_vec<VN>(a.acc + static_cast<size_t>(r0 + r) * d + ch * VN, v);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) v[i] = round_to<T>(v[i]);
+  };
+  tile_inv_rms<VN>(m, d, a.eps, part, inv, h1v);
+  // x = R(RMSNorm(h1) * g_ffn) for rows [0, m) (as in k_mtp_proj)
+  const T *gf = static_cast<const T *>(a.norm_ffn);
+  const int nx = m * nvec;
+  for (int it0 = tid; it0 < nx; it0 += kChunksInFlight * blockDim.x) {
+    float v[kChunksInFlight][VN];
+    uint4 gq[kChunksInFlight];
+#pragma unroll
+    for (int u = 0; u < kChunksInFlight; ++u) {
+      const int it = it0 + u * static_cast<int>(blockDim.x), r = it / nvec, ch = it - r * nvec;
+      if (it < nx) {
+        h1v(r, ch, v[u]);
+        gq[u] = ld16(gf + ch * VN);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunksInFlight; ++u) {
+      const int it = it0 + u * static_cast<int>(blockDim.x), r = it / nvec;
+      if (it >= nx) break;
+      float g[VN], o[VN];
+      unpack(gq[u], g, T());
+#pragma unroll
+      for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[u][i] * inv[r]) * g[i]);
+      st16(A + r * lda + (it - r * nvec) * VN, pack(o, T()));
+    }
+  }
+  __syncthreads();
+  part_w.template finish<false>(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, up_acc, tid);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_dn(ExpertArgs p, MtpArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int rows[kTileM];
+  __shared__ float half_acc[2][64][4];
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63, r0 = blockIdx.y * kTileM;
+  const TileInfo ti{0, r0, min(kTileM, a.B - r0)};
+  DownPart<T, kDenseU> part_w;
+  part_w.begin(p, ti, blockIdx.x, threadIdx.x);
+  if (threadIdx.x < kTileM) rows[threadIdx.x] = r0 + threadIdx.x;
+  stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
+  __syncthreads();
+  part_w.finish(p, ti, reinterpret_cast<const T *>(smem) + (lane & 15) * (p.F + VN) + (lane >> 4) * VN, half_acc,
+                threadIdx.x, rows, nullptr);
+}
+
+// Larger batches (more than kMtpFusedMaxB sequences) normalise in row
+// kernels, one block per sequence, and the projection and gate/up read their
+// tiles from global memory: with 16 rows per tile the in-block norms of the
+// fused kernels would run four rows after one another per wavefront.
+
+// u = [R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e)] of sequence blockIdx.x,
+// with the token and key handling of k_mtp_proj.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_mtp_in(MtpArgs a, int step) {
   constexpr int VN = Vec<T>::N;
@@ -73,35 +226,36 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_in(MtpArgs a, int step) {
   __shared__ int tok;
   const int b = blockIdx.x, d = a.d;
   if (threadIdx.x == 0) {
-    int t;
-    if (step == 0) {
-      t = a.tokens[b];
-    } else {
-      t = static_cast<int>(key_index(a.argkey[b]));
+    const unsigned long long *key_prev = a.argkey + static_cast<size_t>((step - 1) & 1) * a.B;
+    int t = a.tokens[b];
+    if (step > 0) {
+      t = static_cast<int>(key_index(key_prev[b]));
       a.drafts[static_cast<size_t>(b) * a.K + step - 1] = t;
     }
-    a.argkey[b] = 0ull;  // for this step's LM head
+    a.argkey[static_cast<size_t>(step & 1) * a.B + b] = 0ull;
     tok = min(max(t, 0), a.V - 1);
-    a.rows[b] = b;  // the one-expert tile table of the dense kernels
-    if (b == 0) {
-      const int ntiles = (a.B + kTileM - 1) / kTileM;
-      a.tile_start[0] = 0;
-      a.tile_start[1] = ntiles;
-      for (int y = 0; y < ntiles; ++y) a.tile_info[y] = make_int4(0, y * kTileM, min(kTileM, a.B - y * kTileM), 0);
-    }
   }
   __syncthreads();
   const T *h = static_cast<const T *>(step == 0 ? a.h_in : a.h_cur) + static_cast<size_t>(b) * d;
   const T *e = static_cast<const T *>(a.embed) + static_cast<size_t>(tok) * d;
   T *u = static_cast<T *>(a.u) + static_cast<size_t>(b) * 2 * d;
-  auto hv = [&](int ch, float *v) { unpack(ld16(h + ch * VN), v, T()); };
-  auto ev = [&](int ch, float *v) { unpack(ld16(e + ch * VN), v, T()); };
-  const float ih = block_inv_rms<VN>(d, a.eps, part, inv, hv);
-  store_normed<T>(d, ih, static_cast<const T *>(a.norm_h), u, hv);
-  const float ie = block_inv_rms<VN>(d, a.eps, part, inv + 1, ev);
-  store_normed<T>(d, ie, static_cast<const T *>(a.norm_e), u + d, ev);
+  auto hv = [&](int, int ch, float *v) { unpack(ld16(h + ch * VN), v, T()); };
+  auto ev = [&](int, int ch, float *v) { unpack(ld16(e + ch * VN), v, T()); };
+  tile_inv_rms<VN>(1, d, a.eps, part, inv, hv);
+  tile_inv_rms<VN>(1, d, a.eps, part, inv + 1, ev);
+  const T *gh = static_cast<const T *>(a.norm_h), *ge = static_cast<const T *>(a.norm_e);
+  for (int c = threadIdx.x; c < 2 * (d / VN); c += blockDim.x) {
+    const int half = c >= d / VN, ch = c - half * (d / VN);
+    float v[VN], g[VN], o[VN];
+    if (half) ev(0, ch, v); else hv(0, ch, v);
+    unpack(ld16((half ? ge : gh) + ch * VN), g, T());
+#pragma unroll
+    for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[i] * inv[half]) * g[i]);
+    st16(u + c * VN, pack(o, T()));
+  }
 }
 
+// x = R(RMSNorm(R(z)) * g_ffn) of sequence blockIdx.x.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_mtp_mid(MtpArgs a) {
   constexpr int VN = Vec<T>::N;
@@ -109,21 +263,43 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_mid(MtpArgs a) {
   __shared__ float inv;
   const int b = blockIdx.x, d = a.d;
   const float *z = a.acc + static_cast<size_t>(b) * d;
-  T *h1 = static_cast<T *>(a.h1) + static_cast<size_t>(b) * d;
-  auto hv = [&](int ch, float *v) {  // h1 = R(z), recomputed from z on each pass
-    float q[VN];
-    ld_f32<4>(z + ch * VN, q);
-    if (VN == 8) ld_f32<4>(z + ch * VN + 4, q + 4);
+  auto h1v = [&](int, int ch, float *v) {
+    ld_vec<VN>(z + ch * VN, v);
 #pragma unroll
-    for (int i = 0; i < VN; ++i) v[i] = round_to<T>(q[i]);
+    for (int i = 0; i < VN; ++i) v[i] = round_to<T>(v[i]);
   };
+  tile_inv_rms<VN>(1, d, a.eps, part, &inv, h1v);
+  const T *gf = static_cast<const T *>(a.norm_ffn);
+  T *x = static_cast<T *>(a.x) + static_cast<size_t>(b) * d;
   for (int ch = threadIdx.x; ch < d / VN; ch += blockDim.x) {
-    float v[VN];
-    hv(ch, v);
-    st16(h1 + ch * VN, pack(v, T()));
+    float v[VN], g[VN], o[VN];
+    h1v(0, ch, v);
+    unpack(ld16(gf + ch * VN), g, T());
+#pragma unroll
+    for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[i] * inv) * g[i]);
+    st16(x + ch * VN, pack(o, T()));
   }
-  const float ix = block_inv_rms<VN>(d, a.eps, part, &inv, hv);
-  store_normed<T>(d, ix, static_cast<const T *>(a.norm_ffn), static_cast<T *>(a.x) + static_cast<size_t>(b) * d, hv);
+}
+
+// The FFN gate/up of a 16-row tile of x (global).
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void k_mtp_dense_gu(ExpertArgs p, MtpArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float up_acc[2][64][4];
+  constexpr int VN = Vec<T>::N;
+  const int d = a.d, nvec = d / VN, lda = d + VN, lane = threadIdx.x & 63;
+  const int r0 = blockIdx.y * kTileM, m = min(kTileM, a.B - r0);
+  const TileInfo ti{0, r0, m};
+  GateUpPart<T, kDenseU> part_w;
+  part_w.begin(p, ti, blockIdx.x, threadIdx.x);
+  T *A = reinterpret_cast<T *>(smem);
+  const T *x = static_cast<const T *>(a.x);
+  for (int it = threadIdx.x; it < m * nvec; it += blockDim.x) {  // rows [0, m), as in k_mtp_proj
+    const int r = it / nvec, ch = it - r * nvec;
+    st16(A + r * lda + ch * VN, ld16(x + static_cast<size_t>(r0 + r) * d + ch * VN));
+  }
+  __syncthreads();
+  part_w.template finish<false>(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, up_acc, threadIdx.x);
 }
 
 template <typename T>
@@ -132,59 +308,107 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_out(MtpArgs a, int last) {
   __shared__ float part[kMtpMaxD / 4];
   __shared__ float inv;
   const int b = blockIdx.x, d = a.d;
-  const float *y = a.acc + static_cast<size_t>(b) * d;
-  const T *h1 = static_cast<const T *>(a.h1) + static_cast<size_t>(b) * d;
-  auto hv = [&](int ch, float *v) {  // h2 = R(h1 + y)
+  const float *z = a.acc + static_cast<size_t>(b) * d, *y = a.acc2 + static_cast<size_t>(b) * d;
+  auto hv = [&](int, int ch, float *v) {  // h2 = R(R(z) + y)
     float q[VN];
-    ld_f32<4>(y + ch * VN, q);
-    if (VN == 8) ld_f32<4>(y + ch * VN + 4, q + 4);
-    unpack(ld16(h1 + ch * VN), v, T());
+    ld_vec<VN>(z + ch * VN, v);
+    ld_vec<VN>(y + ch * VN, q);
 #pragma unroll
-    for (int i = 0; i < VN; ++i) v[i] = round_to<T>(v[i] + q[i]);
+    for (int i = 0; i < VN; ++i) v[i] = round_to<T>(round_to<T>(v[i]) + q[i]);
   };
   T *hc = static_cast<T *>(a.h_cur) + static_cast<size_t>(b) * d;
   T *ho = last && a.h_out ? static_cast<T *>(a.h_out) + static_cast<size_t>(b) * d : nullptr;
   for (int ch = threadIdx.x; ch < d / VN; ch += blockDim.x) {
     float v[VN];
-    hv(ch, v);
+    hv(0, ch, v);
     const uint4 pk = pack(v, T());
     st16(hc + ch * VN, pk);
     if (ho) st16(ho + ch * VN, pk);
   }
-  const float io = block_inv_rms<VN>(d, a.eps, part, &inv, hv);
-  store_normed<T>(d, io, static_cast<const T *>(a.norm_out), static_cast<T *>(a.xo) + static_cast<size_t>(b) * d, hv);
+  tile_inv_rms<VN>(1, d, a.eps, part, &inv, hv);
+  const T *go = static_cast<const T *>(a.norm_out);
+  T *xo = static_cast<T *>(a.xo) + static_cast<size_t>(b) * d;
+  for (int ch = threadIdx.x; ch < d / VN; ch += blockDim.x) {
+    float v[VN], g[VN], o[VN];
+    hv(0, ch, v);
+    unpack(ld16(go + ch * VN), g, T());
+#pragma unroll
+    for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[i] * inv) * g[i]);
+    st16(xo + ch * VN, pack(o, T()));
+  }
 }
 
 __global__ void k_mtp_last(MtpArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < a.B) a.drafts[static_cast<size_t>(b) * a.K + a.K - 1] = static_cast<int>(key_index(a.argkey[b]));
+  const unsigned long long *key = a.argkey + static_cast<size_t>((a.K - 1) & 1) * a.B;
+  if (b < a.B) a.drafts[static_cast<size_t>(b) * a.K + a.K - 1] = static_cast<int>(key_index(key[b]));
 }
 
 template <typename KernelT>
-hipError_t launch_rows(KernelT kernel, const MtpArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(kernel, dim3(a.B), dim3(kRowThreads), 0, s, a);
-  return hipGetLastError();
+void set_lds(KernelT kernel, size_t bytes) {
+  if (bytes > 48 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(bytes));
 }
 
 }  // namespace
 
-hipError_t launch_mtp_in(int dtype, const MtpArgs &a, int step, hipStream_t s) {
-  if (dtype == 1)
-    hipLaunchKernelGGL(k_mtp_in<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, step);
-  else
-    hipLaunchKernelGGL(k_mtp_in<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, step);
-  return hipGetLastError();
+size_t mtp_proj_lds(int d, int es) {  // the tile and its rows' chunk sums
+  return static_cast<size_t>(kTileM) * (2 * d + 16 / es) * es + static_cast<size_t>(kTileM) * (d / (16 / es)) * 4;
+}
+static size_t mtp_gu_lds(int d, int es) {
+  return static_cast<size_t>(kTileM) * (d + 16 / es) * es + static_cast<size_t>(kTileM) * (d / (16 / es)) * 4;
+}
+size_t mtp_ffn_lds(int d, int F, int es) {
+  const size_t gu = mtp_gu_lds(d, es);
+  const size_t dn = static_cast<size_t>(kTileM) * (F + 16 / es) * es;
+  return gu > dn ? gu : dn;
 }
 
-hipError_t launch_mtp_mid(int dtype, const MtpArgs &a, hipStream_t s) {
-  return dtype == 1 ? launch_rows(k_mtp_mid<bf16_t>, a, s) : launch_rows(k_mtp_mid<float>, a, s);
-}
-
-hipError_t launch_mtp_out(int dtype, const MtpArgs &a, int last, hipStream_t s) {
-  if (dtype == 1)
+hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertArgs &gu, const ExpertArgs &dn,
+                               const MtpArgs &a, int step, hipStream_t s) {
+  const int ntiles = (a.B + kTileM - 1) / kTileM, es = dtype == 1 ? 2 : 4;
+  const dim3 g_proj((a.d + 31) / 32, ntiles), g_gu((gu.F + 31) / 32, ntiles), g_dn((a.d + 31) / 32, ntiles);
+  const size_t l_proj = mtp_proj_lds(a.d, es);
+  const size_t l_gu = mtp_gu_lds(a.d, es);
+  const size_t l_dn = static_cast<size_t>(kTileM) * (dn.F + 16 / es) * es;
+  const int last = step == a.K - 1;
+  const bool fused = a.B <= kMtpFusedMaxB;
+  ExpertArgs proj_u = proj;  // the row-kernel path's projection reads u from global
+  proj_u.a = a.u;
+  if (dtype == 1) {
+    set_lds(k_mtp_proj<bf16_t>, l_proj);
+    set_lds(k_mtp_ffn_gu<bf16_t>, l_gu);
+    set_lds(k_mtp_dense_gu<bf16_t>, l_gu);
+    set_lds(k_mtp_ffn_dn<bf16_t>, l_proj > l_dn ? l_proj : l_dn);
+    if (fused) {
+      hipLaunchKernelGGL(k_mtp_proj<bf16_t>, g_proj, dim3(kRowThreads), l_proj, s, proj, a, step);
+      hipLaunchKernelGGL(k_mtp_ffn_gu<bf16_t>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
+    } else {
+      hipLaunchKernelGGL(k_mtp_in<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, step);
+      hipLaunchKernelGGL(k_mtp_ffn_dn<bf16_t>, g_proj, dim3(kRowThreads), l_proj, s, proj_u, a);
+      hipLaunchKernelGGL(k_mtp_mid<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a);
+      hipLaunchKernelGGL(k_mtp_dense_gu<bf16_t>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
+    }
+    hipLaunchKernelGGL(k_mtp_ffn_dn<bf16_t>, g_dn, dim3(kRowThreads), l_dn, s, dn, a);
     hipLaunchKernelGGL(k_mtp_out<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
-  else
+  } else {
+    set_lds(k_mtp_proj<float>, l_proj);
+    set_lds(k_mtp_ffn_gu<float>, l_gu);
+    set_lds(k_mtp_dense_gu<float>, l_gu);
+    set_lds(k_mtp_ffn_dn<float>, l_proj > l_dn ? l_proj : l_dn);
+    if (fused) {
+      hipLaunchKernelGGL(k_mtp_proj<float>, g_proj, dim3(kRowThreads), l_proj, s, proj, a, step);
+      hipLaunchKernelGGL(k_mtp_ffn_gu<float>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
+    } else {
+      hipLaunchKernelGGL(k_mtp_in<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, step);
+      hipLaunchKernelGGL(k_mtp_ffn_dn<float>, g_proj, dim3(kRowThreads), l_proj, s, proj_u, a);
+      hipLaunchKernelGGL(k_mtp_mid<float>, dim3(a.B), dim3(kRowThreads), 0, s, a);
+      hipLaunchKernelGGL(k_mtp_dense_gu<float>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
+    }
+    hipLaunchKernelGGL(k_mtp_ffn_dn<float>, g_dn, dim3(kRowThreads), l_dn, s, dn, a);
     hipLaunchKernelGGL(k_mtp_out<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
+  }
   return hipGetLastError();
 }
 

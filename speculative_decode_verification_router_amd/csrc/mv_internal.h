@@ -119,32 +119,37 @@ struct LmArgs {
   AcceptArgs accept;
 };
 
-// FastMTP draft block, per-row kernels (k_mtp.hip).  Buffers are [B, ...]
-// rows in the config dtype unless noted.
+// FastMTP draft block (k_mtp.hip).  Buffers are [B, ...] rows in the
+// config dtype unless noted.
 constexpr int kMtpMaxD = 4096;
 struct MtpArgs {
   int B, K, d, V;
   float eps;
-  const int *tokens;             // [B] input tokens (step 0)
-  unsigned long long *argkey;    // [B] LM-head argmax keys
+  const int *tokens;             // [B] input tokens (position 0)
+  unsigned long long *argkey;    // [2, B] LM-head argmax keys, by position parity
   int *drafts;                   // [B, K]
-  int *rows;                     // [B] one-expert tile table of the dense kernels
-  int *tile_start;               // [2]
-  int4 *tile_info;               // [ceil(B / 16)]
-  const void *h_in;              // [B, d] step 0's hidden state
-  void *h_cur;                   // [B, d] the block's output, next step's input
-  void *h_out;                   // [B, d] or null: the last step's output
+  const void *h_in;              // [B, d] position 0's hidden state
+  void *h_cur;                   // [B, d] the block's output, next position's input
+  void *h_out;                   // [B, d] or null: the last position's output
   const void *embed;             // [V, d]
   const void *norm_h, *norm_e, *norm_ffn, *norm_out;  // [d]
-  void *u;                       // [B, 2d] projection input
-  float *acc;                    // [B, d] fp32: projection output, then FFN output
-  void *h1;                      // [B, d] projected hidden state
-  void *x;                       // [B, d] FFN input
+  float *acc;                    // [B, d] fp32 projection output z
+  float *acc2;                   // [B, d] fp32 FFN output y
   void *xo;                      // [B, d] LM-head input
+  void *u;                       // [B, 2d] projection input (row-kernel path)
+  void *x;                       // [B, d] FFN input (row-kernel path)
 };
-hipError_t launch_mtp_in(int dtype, const MtpArgs &a, int step, hipStream_t s);
-hipError_t launch_mtp_mid(int dtype, const MtpArgs &a, hipStream_t s);
-hipError_t launch_mtp_out(int dtype, const MtpArgs &a, int last, hipStream_t s);
+// Up to this many sequences the projection and gate/up kernels normalise
+// their tiles themselves (at most one row per wavefront).
+constexpr int kMtpFusedMaxB = 4;
+// Dynamic LDS of the projection and FFN kernels, bytes (es: element size).
+size_t mtp_proj_lds(int d, int es);
+size_t mtp_ffn_lds(int d, int F, int es);
+// The four launches of one draft position before its LM head; proj, gu and
+// dn are one-expert arguments (E = 1, k = 0, nslot = 1) of the projection
+// (F = 2d, slots = acc), the FFN gate/up (a_out) and the FFN down (slots = acc2).
+hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertArgs &gu, const ExpertArgs &dn,
+                               const MtpArgs &a, int step, hipStream_t s);
 hipError_t launch_mtp_last(const MtpArgs &a, hipStream_t s);
 
 // dtype-dispatched launchers (dtype: 0 fp32, 1 bf16); return the launch error.
@@ -152,10 +157,6 @@ hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int
 hipError_t launch_permute(const RouteArgs &a, hipStream_t s);
 hipError_t launch_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
-// The same 16-row kernels with kUnrollFused windows per weight batch, for
-// grids too small to fill the chip (the draft block's dense layers).
-hipError_t launch_dense_gate_up(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
-hipError_t launch_dense_down(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s);
 // ra / ca: also route this layer inside the launch (kLogits), or null.
 hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra, const CombineArgs *ca, int max_tiles,
                             hipStream_t s);

@@ -152,3 +152,34 @@ def test_draft_verify_accept_loop_is_lossless(bd, torch_cuda, tiny):
         steps += 1
     assert seq[:n] == greedy[1:n + 1]
     print(f"{steps} steps, {accepted} drafts accepted")
+
+
+@pytest.mark.parametrize("B,K", [(1, 3), (17, 2)])
+def test_mtp_draft_in_a_graph(bd, torch_cuda, tiny, B, K):
+    """The draft block captured in a HIP graph: every replay, with eager work
+    on the stream between replays, equals the eager call bit for bit."""
+    torch = torch_cuda
+    dims, W, M, model, mtp = tiny
+    h = bd.to_device(synth.make_hidden(dims, B, code=60 + B))
+    tok = bd.to_device(((np.arange(B) * 31 + 7) % dims.vocab).astype(np.int32))
+    ref = bd.run_mtp_draft(model, mtp, h, tok, K)
+    torch.cuda.synchronize()
+    ref = {k: bd.to_host(v) for k, v in ref.items()}
+    out = bd.run_mtp_draft(model, mtp, h, tok, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bd.mtp_draft(model.cfg, model.weights, mtp.weights, B, K, h, tok, out["drafts"], out["h_out"],
+                     mtp.ws, mtp.ws_bytes, side)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bd.mtp_draft(model.cfg, model.weights, mtp.weights, B, K, h, tok, out["drafts"], out["h_out"],
+                     mtp.ws, mtp.ws_bytes, torch.cuda.current_stream())
+    for rep in range(3):
+        out["drafts"].fill_(-7)        # eager work between replays
+        out["h_out"].fill_(3.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, want in ref.items():
+            assert np.array_equal(bd.to_host(out[key]), want), (rep, key)
