@@ -9,8 +9,8 @@
 //                 u = [R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e)] in LDS
 //                 itself (t: the input token, or the previous draft read from
 //                 the LM head's argmax key), and block (0, 0) records the
-//                 previous draft and clears the key buffer this step's LM
-//                 head will fold into
+//                 previous draft and clears the key buffer this position's
+//                 LM head will fold into
 //   k_mtp_ffn_gu  a = R(SiLU(x Wg^T) * (x Wu^T)), x = R(RMSNorm(R(z)) * g_ffn)
 //                 built in LDS by each block
 //   k_mtp_ffn_dn  y = a W_down^T
@@ -19,12 +19,12 @@
 //
 // and k_mtp_last reads the last draft.  Above kMtpFusedMaxB sequences the
 // norms run in row kernels instead (k_mtp_in, k_mtp_mid; see below).  The
-// argmax keys alternate between two
-// buffers by position parity, so a projection reads the previous position's
-// keys while its block (0, 0) clears the other buffer.  The weight streams are
-// the expert-tile parts of expert_core.h with kUnrollFused windows per batch
-// (these grids are small).  A row's sum of squares is taken per 16-byte chunk
-// in order, then over the chunks as in the verify step's RMSNorm.
+// argmax keys alternate between two buffers by position parity, so a
+// projection reads the previous position's keys while its block (0, 0)
+// clears the other buffer.  The weight streams are the expert-tile parts of
+// expert_core.h with kUnrollFused windows per batch (these grids are small).
+// A row's sum of squares is taken per 16-byte chunk in order, then over the
+// chunks as in the verify step's RMSNorm.
 #include "expert_core.h"
 
 namespace mv {
