@@ -77,6 +77,9 @@ def main(argv=None):
     ap.add_argument("--loop-tokens", type=int, default=1085)
     ap.add_argument("--draft", action="store_true",
                     help="time the FastMTP draft block (mtp_draft) for the workload's B and K")
+    ap.add_argument("--choose-k", action="store_true",
+                    help="time a draft + verify step for K = 0..3 and report the draft length "
+                         "mv_choose_k picks across acceptance rates")
     ap.add_argument("--with-draft", action="store_true",
                     help="decode loop: run the draft block in every step (its cost is timed; the "
                          "committed tokens follow the synthetic drafts of the given p)")
@@ -116,6 +119,8 @@ def main(argv=None):
         line = bench_stack(args, wl, W, bd, synth, torch)
     elif args.draft:
         line = bench_draft(args, wl, W, bd, synth, torch)
+    elif args.choose_k:
+        line = bench_choose_k(args, wl, W, bd, synth, torch)
     elif args.loop:
         line = bench_loop(args, wl, W, bd, synth, torch)
     else:
@@ -459,6 +464,58 @@ def bench_draft(args, wl, W, bd, synth, torch):
                      "algorithmic_bytes_per_step": int(nbytes)},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 4),
+    })
+    return line
+
+
+def bench_choose_k(args, wl, W, bd, synth, torch):
+    """Draft length: the cost of one speculative step (mtp_draft for K
+    positions, then moe_verify_step over B (K + 1) rows) timed for K = 0..3,
+    and the K that mv_choose_k picks from those costs, and from the byte model
+    mv_step_bytes, for a range of per-position acceptance rates."""
+    dims = wl.dims
+    B, k_max = wl.batch, 3
+    model = bd.DeviceModel(dims, W, max_tokens=B * (k_max + 1))
+    M = synth.make_mtp_weights(dims, seed=args.seed, sigma=wl.weight_sigma)
+    mtp = bd.DeviceMtp(dims, M, max_rows=B)
+    h_rows = bd.to_device(synth.make_hidden(dims, B * (k_max + 1), args.seed, wl.code))
+    tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+    cost = []
+    for K in range(k_max + 1):
+        T = B * (K + 1)
+        d_out = torch.empty((B, max(K, 1)), dtype=torch.int32, device="cuda")
+        out = bd.run_verify_step(model, h_rows[:T], d_out, B, K)
+        first = torch.arange(B, device="cuda") * (K + 1)
+
+        def step(stream, K=K, T=T, d_out=d_out, out=out, first=first):
+            if K:
+                bd.mtp_draft(model.cfg, model.weights, mtp.weights, B, K, h_rows.index_select(0, first), tok,
+                             d_out, None, mtp.ws, mtp.ws_bytes, stream)
+            bd.moe_verify_step(model.cfg, model.weights, B, K, h_rows[:T], d_out, out["h_out"], out["argmax"],
+                               out["n_accepted"], out["committed"], out["n_committed"], None, model.ws,
+                               model.ws_bytes, stream)
+
+        ms, _, _ = _timed(step, torch.cuda.current_stream(), args.steps, args.warmup, torch)
+        cost.append(ms)
+    nbytes = [bd.mv_step_bytes(model.cfg, B, K, mtp.d_ff) for K in range(k_max + 1)]
+    table = []
+    for q in (0.3, 0.4, 0.5, 0.576, 0.6, 0.7, 0.7485, 0.8, 0.9):
+        k_t, r_t = bd.mv_choose_k(q, cost)
+        k_b, _ = bd.mv_choose_k(q, [b / 1e9 for b in nbytes])
+        table.append({"q": q, "k_time": k_t, "tok_per_s": round(B * r_t * 1e3, 1), "k_bytes": k_b})
+    q0 = wl.match_p + (1 - wl.match_p) / dims.vocab
+    k0, r0 = bd.mv_choose_k(q0, cost)
+    line = {"metric": "committed tokens/s at the draft length chosen from measured step costs",
+            "value": round(B * r0 * 1e3, 1), "unit": "committed tokens/s (expected)"}
+    line.update(_header(args, wl))
+    line.update({
+        "ms_per_step": round(cost[k0], 4),
+        "data": "synthetic (seeded; weights N(0,0.02)); expected commits 1 + q + ... + q^K",
+        "config": {"workload": wl.name + "_choose_k", "batch": B, "k_max": k_max, "q": round(q0, 4),
+                   "chosen_k": k0, "step_ms": [round(c, 4) for c in cost],
+                   "step_gb_model": [round(b / 1e9, 4) for b in nbytes], "policy": table},
+        "roofline": None,
+        "cpu_baseline": None,
     })
     return line
 

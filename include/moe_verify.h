@@ -202,6 +202,28 @@ int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weights *m, i
               int32_t K, const void *h_in, const int32_t *tokens, int32_t *drafts,
               void *h_out, void *ws, size_t ws_bytes, void *stream);
 
+/* Draft length for the next speculative step (FastMTP paragraph of the
+ * ainewsfeed page: the best K depends on acceptance and on what a step
+ * costs).  With K drafts, each accepted independently with probability q,
+ * the accept rule commits E(K) = 1 + q + ... + q^K tokens per sequence on
+ * average; the chosen K in [0, k_max] maximises E(K) / cost[K], the smallest
+ * K on ties.  cost[K] (host memory, k_max + 1 values, each > 0) is the cost
+ * of one step with K drafts in any unit: measured time, or mv_step_bytes.
+ *   k_best  the chosen K;  rate  E(k_best) / cost[k_best] (NULL to skip)
+ * Host-only, pure.  Errors: MV_ERR_NULL, MV_ERR_SHAPE (k_max outside
+ * [0, 15], q outside [0, 1], a cost not > 0). */
+int mv_choose_k(int32_t k_max, float q, const float *cost, int32_t *k_best, float *rate);
+
+/* Expected HBM bytes of one speculative step for B sequences with K drafts:
+ * K positions of the draft block (its matrices, the LM head, four norm
+ * vectors, and per sequence the embedding row and hidden rows in and out;
+ * d_ff_mtp = 0 for no draft block), then moe_verify_step over T = B (K+1)
+ * rows (all routed experts the rows choose, with uniform routing an expert
+ * is chosen by some row with probability 1 - (1 - top_k / n_routed)^T; the
+ * shared experts, router and norm vectors, the LM head, the rows in and
+ * out).  Host-only, pure; a negative value on invalid arguments. */
+double mv_step_bytes(const mv_config *cfg, int32_t B, int32_t K, int32_t d_ff_mtp);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char *mv_last_error(void);
 

@@ -340,3 +340,49 @@ def mtp_draft(h_in: np.ndarray, tokens: np.ndarray, M: Dict[str, np.ndarray], W,
     B = h.shape[0]
     return dict(drafts=np.stack(drafts, 1) if K else np.zeros((B, 0), np.int64), h_out=h,
                 margin=np.stack(margins, 1) if K else np.zeros((B, 0)))
+
+
+# ---------------------------------------------------------------------------
+# draft length
+# ---------------------------------------------------------------------------
+
+
+def expected_committed(q: float, K: int) -> float:
+    """Expected tokens committed per sequence and step with K drafts, each
+    accepted independently with probability q: the accept rule commits the
+    accepted prefix n plus one token, and P(n >= i) = q^i, so
+    E[n + 1] = 1 + q + ... + q^K."""
+    return float(sum(q ** i for i in range(K + 1)))
+
+
+def choose_k(q: float, cost) -> tuple:
+    """Draft length K in [0, len(cost)) with the most expected committed
+    tokens per unit of cost (cost[K]: time or bytes of a step with K drafts);
+    the smallest K on ties.  Returns (K, rate)."""
+    rates = [expected_committed(q, K) / float(c) for K, c in enumerate(cost)]
+    best = max(range(len(rates)), key=lambda K: (rates[K], -K))
+    return best, rates[best]
+
+
+def expected_distinct_experts(T: int, E: int, k: int) -> float:
+    """Expected number of distinct experts chosen by T tokens that each pick
+    k of E experts uniformly without replacement: an expert is missed by one
+    token with probability 1 - k/E, by all T with (1 - k/E)^T."""
+    return E * (1.0 - (1.0 - k / E) ** T)
+
+
+def step_bytes(dims, B: int, K: int, d_ff_mtp: int) -> float:
+    """Expected HBM bytes of one speculative step: K positions of the draft
+    block (its matrices, the LM head, four norm vectors, and per sequence the
+    embedding row and hidden rows in and out), then the verify step over
+    T = B (K + 1) rows (the routed experts the tokens choose under uniform
+    routing, the shared experts, router and norm vectors, the LM head and
+    the hidden rows in and out)."""
+    es = 2 if dims.dtype == "bf16" else 4
+    d, F, E, S, L, V = dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared, dims.n_layers, dims.vocab
+    T = B * (K + 1)
+    expert = 3 * F * d * es
+    verify = L * (expected_distinct_experts(T, E, dims.top_k) + S) * expert
+    verify += L * (E * d + d) * es + V * d * es + d * es + 2 * T * d * es
+    draft = K * ((2 * d * d + 3 * d_ff_mtp * d + V * d + 4 * d) * es + B * 3 * d * es)
+    return float(verify + draft)

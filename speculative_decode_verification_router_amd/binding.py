@@ -20,7 +20,7 @@ MV_F32, MV_BF16 = 0, 1
 MV_OK, MV_ERR_NULL, MV_ERR_SHAPE, MV_ERR_UNSUPPORTED, MV_ERR_WORKSPACE, MV_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("mv_workspace_bytes", "moe_layer_forward", "moe_verify_step", "spec_accept",
-            "mtp_workspace_bytes", "mtp_draft", "mv_last_error")
+            "mtp_workspace_bytes", "mtp_draft", "mv_choose_k", "mv_step_bytes", "mv_last_error")
 
 
 class MvConfig(ctypes.Structure):
@@ -73,6 +73,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtp_workspace_bytes.restype = SZ
     lib.mtp_draft.argtypes = [cfgp, wp, mwp, I, I, P, P, P, P, P, SZ, P]
     lib.mtp_draft.restype = ctypes.c_int
+    lib.mv_choose_k.argtypes = [I, ctypes.c_float, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I),
+                                ctypes.POINTER(ctypes.c_float)]
+    lib.mv_choose_k.restype = ctypes.c_int
+    lib.mv_step_bytes.argtypes = [cfgp, I, I, I]
+    lib.mv_step_bytes.restype = ctypes.c_double
     lib.mv_last_error.argtypes = []
     lib.mv_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -155,6 +160,23 @@ def mtp_draft(cfg: MvConfig, weights: MvWeights, mtp: MtpWeights, B: int, K: int
     _check(load().mtp_draft(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(mtp), B, K,
                             _ptr(h_in), _ptr(tokens), _ptr(drafts), _ptr(h_out), _ptr(ws),
                             ws_bytes, _stream(stream)))
+
+
+def mv_choose_k(q: float, cost) -> tuple:
+    """(K, rate): the draft length with the most expected committed tokens
+    per unit of cost, cost[K] for K = 0 .. len(cost) - 1."""
+    c = (ctypes.c_float * len(cost))(*[float(x) for x in cost])
+    k = ctypes.c_int32(-1)
+    r = ctypes.c_float(0.0)
+    _check(load().mv_choose_k(len(cost) - 1, float(q), c, ctypes.byref(k), ctypes.byref(r)))
+    return int(k.value), float(r.value)
+
+
+def mv_step_bytes(cfg: MvConfig, B: int, K: int, d_ff_mtp: int) -> float:
+    v = float(load().mv_step_bytes(ctypes.byref(cfg), int(B), int(K), int(d_ff_mtp)))
+    if v < 0:
+        raise MvError(MV_ERR_SHAPE, mv_last_error())
+    return v
 
 
 # ---------------------------------------------------------------- device memory

@@ -2,6 +2,7 @@
 // carving and the launch sequence on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -562,6 +563,50 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
       return rc;
   }
   return hip_status(mv::launch_mtp_last(a, s));
+}
+
+// ------------------------------------------------------------- draft length
+
+MV_API int mv_choose_k(int32_t k_max, float q, const float *cost, int32_t *k_best, float *rate) {
+  g_err.clear();
+  if (!cost || !k_best) return fail(MV_ERR_NULL, "cost and k_best are required");
+  if (k_max < 0 || k_max > kMaxK) return fail(MV_ERR_SHAPE, "k_max must be in [0, 15]");
+  if (!(q >= 0.f && q <= 1.f)) return fail(MV_ERR_SHAPE, "q must be in [0, 1]");
+  for (int k = 0; k <= k_max; ++k)
+    if (!(cost[k] > 0.f)) return fail(MV_ERR_SHAPE, "every cost must be > 0");
+  // E(K) = sum_{i <= K} q^i, accumulated in double
+  double e = 0.0, qi = 1.0, best_rate = -1.0;
+  int best = 0;
+  for (int k = 0; k <= k_max; ++k) {
+    e += qi;
+    qi *= static_cast<double>(q);
+    const double r = e / static_cast<double>(cost[k]);
+    if (r > best_rate) {
+      best_rate = r;
+      best = k;
+    }
+  }
+  *k_best = best;
+  if (rate) *rate = static_cast<float>(best_rate);
+  return MV_OK;
+}
+
+MV_API double mv_step_bytes(const mv_config *cfg, int32_t B, int32_t K, int32_t d_ff_mtp) {
+  g_err.clear();
+  if (check_config(cfg) != MV_OK) return -1.0;
+  if (B < 0 || K < 0 || K > kMaxK || d_ff_mtp < 0) {
+    g_err = "B, K and d_ff_mtp must be >= 0 and K <= 15";
+    return -1.0;
+  }
+  const double es = cfg->dtype == MV_BF16 ? 2.0 : 4.0, d = cfg->d_model, F = cfg->d_ff, E = cfg->n_routed;
+  const double V = cfg->vocab, L = cfg->n_layers, T = static_cast<double>(B) * (K + 1);
+  const double miss = std::pow(1.0 - static_cast<double>(cfg->top_k) / E, T);
+  const double distinct = E * (1.0 - miss);
+  double bytes = L * (distinct + cfg->n_shared) * 3.0 * F * d * es;  // routed and shared experts
+  bytes += L * (E * d + d) * es + V * d * es + d * es;               // router, norms, LM head
+  bytes += 2.0 * T * d * es;                                         // rows in and out
+  bytes += K * ((2.0 * d * d + 3.0 * d_ff_mtp * d + V * d + 4.0 * d) * es + B * 3.0 * d * es);  // draft block
+  return bytes;
 }
 
 MV_API const char *mv_last_error(void) { return g_err.c_str(); }
