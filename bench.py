@@ -85,6 +85,9 @@ def main(argv=None):
                          "committed tokens follow the synthetic drafts of the given p)")
     ap.add_argument("--k-draft", type=int, default=None)
     ap.add_argument("--match-p", type=float, default=None)
+    ap.add_argument("--cold", action="store_true",
+                    help="verify step and stack: time each step alone after a 1 GiB cache scrub "
+                         "and report the median")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device copies of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -138,10 +141,34 @@ def _cores():
         return os.cpu_count() or 1
 
 
-def _timed(run, stream, steps, warmup, torch):
-    """Warm up, then time `steps` calls of run(stream) with events on `stream`."""
+SCRUB_BYTES = 1 << 30
+
+
+def _timed(run, stream, steps, warmup, torch, cold=False):
+    """Warm up, then time `steps` calls of run(stream) with events on `stream`.
+
+    cold: before every step a 1 GiB device copy (512 MiB read, 512 MiB
+    written, outside the events) evicts the step's data from L2 and the 256 MB
+    memory-side cache; each step is timed alone and the median is returned."""
     for _ in range(warmup):
         run(stream)
+    if cold:
+        src = torch.ones(SCRUB_BYTES // 2, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for a, b in evs:
+                dst.copy_(src)
+                a.record(stream)
+                run(stream)
+                b.record(stream)
+        t_enq = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return float(np.median([a.elapsed_time(b) for a, b in evs])), wall, t_enq
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -154,6 +181,12 @@ def _timed(run, stream, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return ev0.elapsed_time(ev1) / steps, wall, t_enq
+
+
+def _timing(args):
+    if args.cold:
+        return "cold: median of steps timed alone, each after a 1 GiB cache scrub"
+    return "warm: back-to-back steps between two events"
 
 
 def _header(args, wl):
@@ -198,7 +231,7 @@ def bench_verify(args, wl, W, bd, synth, torch):
             step(torch.cuda.current_stream())
         run = lambda stream: graph.replay()  # noqa: E731
     stream = torch.cuda.current_stream()
-    ms, wall, t_enq = _timed(run, stream, args.steps, args.warmup, torch)
+    ms, wall, t_enq = _timed(run, stream, args.steps, args.warmup, torch, cold=args.cold)
     committed_per_step = int(bd.to_host(out["n_committed"]).sum())
     value = committed_per_step / (ms * 1e-3)
 
@@ -231,6 +264,7 @@ def bench_verify(args, wl, W, bd, synth, torch):
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_ms_per_step": round(t_enq / args.steps * 1e3, 4),
         "graph": bool(args.graph),
+        "timing": _timing(args),
     })
     return line
 
@@ -259,7 +293,7 @@ def bench_stack(args, wl, W, bd, synth, torch):
                                  None, None, None, model.ws, model.ws_bytes, stream)
 
     stream = torch.cuda.current_stream()
-    ms, wall, t_enq = _timed(step, stream, args.steps, args.warmup, torch)
+    ms, wall, t_enq = _timed(step, stream, args.steps, args.warmup, torch, cold=args.cold)
     flops = stack_flops(dims, T)
     achieved = flops / (ms * 1e-3) / 1e12
     cpu = None
@@ -290,6 +324,7 @@ def bench_stack(args, wl, W, bd, synth, torch):
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_ms_per_step": round(t_enq / args.steps * 1e3, 4),
+        "timing": _timing(args),
     })
     return line
 
