@@ -23,7 +23,9 @@ namespace {
 
 constexpr int kRLTok = 16;       // tokens per routing block
 constexpr int kRLThreads = 512;  // 8 wavefronts: 2 expert halves x 4 K quarters
-constexpr int kRLQuarterWin = 20;  // K windows per quarter held in registers (all of them for d <= 1280)
+// K windows per quarter prefetched into registers (half a quarter at d = 1280;
+// the rest is read in the MFMA loop): 110 VGPRs, so two blocks share a CU
+constexpr int kRLQuarterWin = 10;
 constexpr int kScatterThreads = 256;
 
 struct RLSmem {
@@ -34,8 +36,11 @@ __host__ __device__ inline RLSmem rl_smem(int d) {
   RLSmem s;
   s.x = 0;                                                         // [17][d + 8] bf16: rows, then a zero row
   s.p = s.x + static_cast<size_t>(kRLTok + 1) * (d + 8) * 2;       // [16][nvec] fp32 chunk partials
-  s.lg = s.p + static_cast<size_t>(kRLTok) * nvec * 4;             // [4][16][64] fp32 logit quarters
-  s.key = s.lg + static_cast<size_t>(4) * kRLTok * 64 * 4;         // [16][64] top-k keys
+  // [4][16][64] fp32 logit quarters, over the partials: those are read
+  // before the block barriers that precede the logits
+  s.lg = s.p;
+  const size_t p_bytes = static_cast<size_t>(kRLTok) * nvec * 4, lg_bytes = static_cast<size_t>(4) * kRLTok * 64 * 4;
+  s.key = s.lg + (p_bytes > lg_bytes ? p_bytes : lg_bytes);        // [16][64] top-k keys
   s.inv = s.key + static_cast<size_t>(kRLTok) * 64 * 8;            // [16]
   s.sel = s.inv + kRLTok * 4;                                      // [16][kMaxTopK]
   s.g = s.sel + kRLTok * kMaxTopK * 4;                             // [d] gamma, bf16
