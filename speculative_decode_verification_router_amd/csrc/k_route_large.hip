@@ -27,6 +27,7 @@ constexpr int kRLThreads = 512;  // 8 wavefronts: 2 expert halves x 4 K quarters
 // the rest is read in the MFMA loop): 110 VGPRs, so two blocks share a CU
 constexpr int kRLQuarterWin = 10;
 constexpr int kScatterThreads = 256;
+constexpr int kScatterBatch = 32;  // count loads in flight per thread (16.9 -> 14.5 us over 8)
 
 struct RLSmem {
   size_t x, p, lg, key, inv, sel, g, total;
@@ -171,12 +172,12 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(RouteArgs a, const 
     const int e = tid & 63, part = tid >> 6;
     const int b0 = part * nblk / 4, b1 = (part + 1) * nblk / 4;
     int tot = 0, before = 0;
-    for (int b = b0; b < b1; b += 8) {
-      int c[8];  // eight loads in flight per thread
+    for (int b = b0; b < b1; b += kScatterBatch) {
+      int c[kScatterBatch];  // loads in flight per thread
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = b + u < b1 ? blk_cnt[(b + u) * 64 + e] : 0;
+      for (int u = 0; u < kScatterBatch; ++u) c[u] = b + u < b1 ? blk_cnt[(b + u) * 64 + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kScatterBatch; ++u) {
         tot += c[u];
         before += b + u < static_cast<int>(blockIdx.x) ? c[u] : 0;
       }
