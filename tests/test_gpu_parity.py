@@ -140,7 +140,10 @@ def test_layer_forward_tiny_fp32(bd, torch_cuda, tiny, T):
     _layer_check(bd, torch_cuda, dims, W, model, 0, h, f"tiny T={T}")
 
 
-@pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5), (200, 3), (600, 7)])
+# 128 / 129 and 512 / 513 sit on either side of a batch-path switch (16-row
+# tiles, 64-row tiles, 256-row GEMM tiles); 513 leaves the GEMM a one-row tile.
+@pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5), (129, 2), (200, 3), (512, 4), (513, 9),
+                                     (600, 7)])
 def test_layer_forward_bf16_full_width(bd, torch_cuda, big, T, layer):
     dims, W, model = big
     h = synth.make_hidden(dims, T, seed=200 + T)
