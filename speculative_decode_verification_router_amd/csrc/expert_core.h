@@ -63,6 +63,27 @@ __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b,
   }
 }
 
+// The same MFMAs in the same order with two weight batches in flight: batch
+// i + 1 is requested before the MFMAs of batch i (q0 holds the first batch).
+template <typename T, int U>
+__device__ __forceinline__ void mfma_panel2(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
+                                            uint4 *q0, uint4 *q1) {
+  constexpr int W = 4 * Vec<T>::N;
+  auto mma = [&](const uint4 *q, int w0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+  };
+  for (int w0 = w_lo; w0 < w_hi; w0 += 2 * U) {
+    if (w0 + U < w_hi) load_batch<T, U>(q1, b, w0 + U, w_hi);
+    mma(q0, w0);
+    if (w0 + U < w_hi) {
+      if (w0 + 2 * U < w_hi) load_batch<T, U>(q0, b, w0 + 2 * U, w_hi);
+      mma(q1, w0 + U);
+    }
+  }
+}
+
 // The tile's a rows (zero-filled past m) into LDS, row stride F + one vector.
 // kCoherent: a was written by other blocks of the same launch (write-through
 // stores), so it is read with agent-scope loads, which no stale cache line
@@ -107,11 +128,13 @@ __device__ __forceinline__ void store_through(bf16_t *p, float v, int lane) {
 // gate/up of slice pair `pair` of a tile.  begin() issues the first weight
 // batch; finish() runs the MFMAs with this lane's A row at `arow` (LDS),
 // exchanges the up accumulators and writes a (one block barrier inside).
-template <typename T, int U = kUnroll>
+// DB: two weight batches in flight (U more registers).
+template <typename T, int U = kUnroll, bool DB = false>
 struct GateUpPart {
   const T *b;
   int f0, which, slice, nwin;
   uint4 q[U];
+  uint4 q2[DB ? U : 1];  // second weight buffer (DB: two batches in flight)
   __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid) {
     constexpr int VN = Vec<T>::N;
     const int lane = tid & 63, wv = tid >> 6;
@@ -131,7 +154,8 @@ struct GateUpPart {
                                          float (*up_acc)[64][4], int tid) {
     const int lane = tid & 63, F = p.F;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    mfma_panel<T, U>(acc, arow, b, 0, nwin, q);
+    if constexpr (DB) mfma_panel2<T, U>(acc, arow, b, 0, nwin, q, q2);
+    else mfma_panel<T, U>(acc, arow, b, 0, nwin, q);
     if (which == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) up_acc[slice][lane][i] = acc[i];

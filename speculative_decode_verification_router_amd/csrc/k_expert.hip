@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   if (small ? !small_tile<kIdLoads>(p, p.ids, blockIdx.y, ti, st, first && threadIdx.x < kWave)
             : !table_tile(p, blockIdx.y, ti))
     return;
-  GateUpPart<T, U> part;
+  GateUpPart<T, U, true> part;  // two weight batches in flight (the x tile's LDS, not registers, bounds occupancy)
   part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while x is staged
 
   const int d = p.d, nvec = d / VN, lda = d + VN;
