@@ -260,6 +260,56 @@ def test_verify_c32_k3_sampled(bd, torch_cuda, big):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,sample", [(2, None), (4, None), (64, [0, 1, 62, 63, 64, 65, 126, 127])])
+def test_verify_k1_teacher_forced(bd, torch_cuda, big, B, sample):
+    """One draft per sequence at full width: B = 2, 4 (the fused expert launch
+    on up to 8 rows) and B = 64 (128 rows of 16-row tiles).  Every layer is
+    checked on the GPU's own input to it: the oracle's layer fed the GPU's
+    hidden state must route like the GPU (single-layer near-tie rule) and
+    agree on the output rows; the oracle's LM head on the GPU's final hidden
+    state must give the GPU's argmax; the accept rule on the GPU's argmax must
+    give its commits.  Chained moe_layer_forward calls reproduce the verify
+    step's routing and hidden state bit for bit (the same per-row arithmetic
+    on every path up to 512 rows)."""
+    torch = torch_cuda
+    dims, W, model = big
+    K = 1
+    T = B * (K + 1)
+    h0 = synth.make_hidden(dims, T, seed=700 + B)
+    zero = np.zeros((B, K), np.int32)
+    pre = bd.run_verify_step(model, _dev(bd, h0), _dev(bd, zero), B, K, routing=True)
+    _sync(torch)
+    drafts = synth.make_drafts(_host(bd, pre["argmax"]).reshape(B, K + 1), 0.6, dims.vocab, seed=4)
+    out = bd.run_verify_step(model, _dev(bd, h0), _dev(bd, drafts), B, K, routing=True)
+    _sync(torch)
+    ids_verify = _host(bd, out["topk_ids"])
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    tally = Tally(len(rows))
+    hd = _dev(bd, h0)
+    for layer in range(dims.n_layers):
+        lo = bd.run_layer_forward(model, layer, hd)
+        _sync(torch)
+        gid = _host(bd, lo["topk_ids"])
+        assert np.array_equal(gid, ids_verify[layer]), f"layer {layer}: chain and verify step route differently"
+        ref = O.moe_layer(O.widen(_host(bd, hd), dims.dtype)[rows], W, layer, dims)
+        tally.routing(layer, gid[rows], ref["ids"], ref["margin"])
+        tally.rows(f"layer {layer} h_out", O.widen(_host(bd, lo["h_out"]), dims.dtype)[rows], ref["h_out"],
+                   TOL[dims.dtype])
+        hd = lo["h_out"]
+    assert np.array_equal(_host(bd, hd), _host(bd, out["h_out"]))
+    g = _host(bd, out["argmax"])
+    lm = O.lm_head_argmax(O.widen(_host(bd, hd), dims.dtype)[rows], W["final_norm"], W["lm_head"], dims)
+    tally.argmax(g[rows], lm["argmax"], lm["margin"])
+    r_acc, r_com, r_ncom = O.spec_accept(g.reshape(B, K + 1), drafts)
+    assert np.array_equal(_host(bd, out["n_accepted"]), r_acc)
+    assert np.array_equal(_host(bd, out["committed"]), r_com)
+    assert np.array_equal(_host(bd, out["n_committed"]), r_ncom)
+    print(f"verify B={B} K=1 teacher-forced: near-ties {tally.near_ties}, "
+          f"checked tokens {len(rows) - int(tally.excluded.sum())}/{len(rows)}")
+    tally.assert_ok(f"verify B={B} K=1")
+
+
+@pytest.mark.timeout(600)
 def test_verify_large_batch_sampled(bd, torch_cuda, big):
     """150 sequences x 4 rows: the LDS-tiled GEMM path with the combine in
     the shared experts' down projection; the oracle checks sampled sequences."""
