@@ -260,10 +260,11 @@ def test_verify_c32_k3_sampled(bd, torch_cuda, big):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("B,sample", [(2, None), (4, None), (64, [0, 1, 62, 63, 64, 65, 126, 127])])
-def test_verify_k1_teacher_forced(bd, torch_cuda, big, B, sample):
-    """One draft per sequence at full width: B = 2, 4 (the fused expert launch
-    on up to 8 rows) and B = 64 (128 rows of 16-row tiles).  Every layer is
+@pytest.mark.parametrize("B,K,sample", [(2, 1, None), (4, 1, None), (64, 1, [0, 1, 62, 63, 64, 65, 126, 127]),
+                                        (1, 3, None), (32, 3, [0, 1, 2, 3, 60, 61, 62, 63, 124, 125, 126, 127])])
+def test_verify_teacher_forced(bd, torch_cuda, big, B, K, sample):
+    """Full width, one or three drafts per sequence: up to 8 rows (the fused
+    expert launch) and 128 rows (16-row tiles; sampled rows).  Every layer is
     checked on the GPU's own input to it: the oracle's layer fed the GPU's
     hidden state must route like the GPU (single-layer near-tie rule) and
     agree on the output rows; the oracle's LM head on the GPU's final hidden
@@ -273,9 +274,8 @@ def test_verify_k1_teacher_forced(bd, torch_cuda, big, B, sample):
     on every path up to 512 rows)."""
     torch = torch_cuda
     dims, W, model = big
-    K = 1
     T = B * (K + 1)
-    h0 = synth.make_hidden(dims, T, seed=700 + B)
+    h0 = synth.make_hidden(dims, T, seed=700 + B + 10 * K)
     zero = np.zeros((B, K), np.int32)
     pre = bd.run_verify_step(model, _dev(bd, h0), _dev(bd, zero), B, K, routing=True)
     _sync(torch)
@@ -304,9 +304,9 @@ def test_verify_k1_teacher_forced(bd, torch_cuda, big, B, sample):
     assert np.array_equal(_host(bd, out["n_accepted"]), r_acc)
     assert np.array_equal(_host(bd, out["committed"]), r_com)
     assert np.array_equal(_host(bd, out["n_committed"]), r_ncom)
-    print(f"verify B={B} K=1 teacher-forced: near-ties {tally.near_ties}, "
+    print(f"verify B={B} K={K} teacher-forced: near-ties {tally.near_ties}, "
           f"checked tokens {len(rows) - int(tally.excluded.sum())}/{len(rows)}")
-    tally.assert_ok(f"verify B={B} K=1")
+    tally.assert_ok(f"verify B={B} K={K}")
 
 
 @pytest.mark.timeout(600)
