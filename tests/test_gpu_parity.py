@@ -332,11 +332,18 @@ def test_prefill_stack_sampled(bd, torch_cuda, big):
     sample = np.concatenate([sample, [0, T - 1]])
     ht = _dev(bd, h)
     ids = []
+    forced = Tally(len(sample))  # each layer on the GPU's own input (single-layer near-tie rule)
     for layer in range(dims.n_layers):
+        h_in = O.widen(_host(bd, ht), "bf16")[sample]
         out = bd.run_layer_forward(model, layer, ht)
         ids.append(out["topk_ids"])
         ht = out["h_out"]
+        ref_l = O.moe_layer(h_in, W, layer, dims)
+        forced.routing(layer, _host(bd, out["topk_ids"])[sample], ref_l["ids"], ref_l["margin"])
+        forced.rows(f"prefill layer {layer} (teacher-forced)", O.widen(_host(bd, ht), "bf16")[sample],
+                    ref_l["h_out"], TOL["bf16"])
     _sync(torch_cuda)
+    forced.assert_ok("prefill, teacher-forced")
     ref = O.forward_tokens(h[sample], W, dims, lm_head=False)
     ref32 = O.forward_tokens(h[sample], W, dims, lm_head=False, ftype=np.float32)
     cond_layers, _ = stack_conditioning(ref, ref32)
