@@ -46,7 +46,7 @@ constexpr int kGMT = kGWaveM / 32;        // 32-row MFMA tiles per wavefront
 constexpr int kGThreads = 64 * kGWavesM * kGWavesN;
 constexpr int kGWaveN = kGBN / kGWavesN;  // B rows per wavefront
 constexpr int kGChunks = kGBK / 8;    // 16-byte chunks per row and K-step
-constexpr int kGroupTiles = 4;        // row tiles walked together per expert
+constexpr int kGroupTiles = 1;        // row tiles walked together per expert (1 beat 2, 3, 4 and 8)
 constexpr int kXcds = 8;
 
 struct GemmSmem {
@@ -56,7 +56,8 @@ struct GemmSmem {
 
 // Work item of this block: the row tile and column block, or false.  Items
 // of one expert are walked in groups of kGroupTiles row tiles, column block
-// by column block, so the blocks in flight on an XCD share both operands.
+// by column block, so the blocks in flight on an XCD share operands (with one
+// row tile per group: a row tile's activations across its column blocks).
 __device__ bool gemm_item(const int *tile_start, int ne, int nb_count, int &tile, int &nb) {
   const int total = tile_start[ne] * nb_count;
   const int q = (total + kXcds - 1) / kXcds;
