@@ -224,6 +224,27 @@ int mv_choose_k(int32_t k_max, float q, const float *cost, int32_t *k_best, floa
  * out).  Host-only, pure; a negative value on invalid arguments. */
 double mv_step_bytes(const mv_config *cfg, int32_t B, int32_t K, int32_t d_ff_mtp);
 
+/* Status of the last moe_verify_step or moe_layer_forward call made on the
+ * workspace ws.  Calls of up to 8 token rows run each layer's routing, gate/up
+ * and down in one launch, whose blocks wait on counters that blocks of lower
+ * index raise; those blocks are dispatched first, so the waits end.  Each
+ * wait is nonetheless bounded (mv_set_spin_limit): one that gives up lets
+ * its block go on with whatever data it finds, and records 1 in a status
+ * word at offset 0 of the workspace, which the first launch of every call
+ * clears.  This call enqueues, on `stream`, a copy of that word into
+ * status[0] (device memory, int32): 0 means every wait of the call ended as
+ * it should; 1 means the call's results must not be used.  Errors:
+ * MV_ERR_NULL, MV_ERR_WORKSPACE (ws not 256-byte aligned). */
+int mv_step_status(const void *ws, int32_t *status, void *stream);
+
+/* Test hook for the bounded waits above: the number of polls (each about a
+ * microsecond) a wait makes before it gives up, for calls enqueued after
+ * this one, process-wide.  polls < 0 restores the default (2^18); polls = 0
+ * makes every wait that finds its counter short give up at once.  Returns
+ * the previous limit.  Host-only; every kernel still runs to its end
+ * whatever the limit. */
+int32_t mv_set_spin_limit(int32_t polls);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char *mv_last_error(void);
 

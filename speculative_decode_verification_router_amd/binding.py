@@ -20,7 +20,8 @@ MV_F32, MV_BF16 = 0, 1
 MV_OK, MV_ERR_NULL, MV_ERR_SHAPE, MV_ERR_UNSUPPORTED, MV_ERR_WORKSPACE, MV_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("mv_workspace_bytes", "moe_layer_forward", "moe_verify_step", "spec_accept",
-            "mtp_workspace_bytes", "mtp_draft", "mv_choose_k", "mv_step_bytes", "mv_last_error")
+            "mtp_workspace_bytes", "mtp_draft", "mv_choose_k", "mv_step_bytes", "mv_step_status",
+            "mv_set_spin_limit", "mv_last_error")
 
 
 class MvConfig(ctypes.Structure):
@@ -78,6 +79,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mv_choose_k.restype = ctypes.c_int
     lib.mv_step_bytes.argtypes = [cfgp, I, I, I]
     lib.mv_step_bytes.restype = ctypes.c_double
+    lib.mv_step_status.argtypes = [P, P, P]
+    lib.mv_step_status.restype = ctypes.c_int
+    lib.mv_set_spin_limit.argtypes = [I]
+    lib.mv_set_spin_limit.restype = I
     lib.mv_last_error.argtypes = []
     lib.mv_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -179,6 +184,17 @@ def mv_step_bytes(cfg: MvConfig, B: int, K: int, d_ff_mtp: int) -> float:
     return v
 
 
+def mv_step_status(ws, status, stream=None) -> None:
+    """Enqueue the copy of workspace ws's status word into status[0] (int32)."""
+    _check(load().mv_step_status(_ptr(ws), _ptr(status), _stream(stream)))
+
+
+def mv_set_spin_limit(polls: int) -> int:
+    """Bound of the fused launch's waits for later calls (< 0: the default);
+    returns the previous bound."""
+    return int(load().mv_set_spin_limit(int(polls)))
+
+
 # ---------------------------------------------------------------- device memory
 
 
@@ -242,6 +258,16 @@ def run_mtp_draft(model: DeviceModel, mtp: DeviceMtp, h_in, tokens, K: int, stre
     mtp_draft(model.cfg, model.weights, mtp.weights, B, K, h_in, tokens, out["drafts"],
               out["h_out"], mtp.ws, mtp.ws_bytes, stream)
     return out
+
+
+def step_status(model: "DeviceModel", stream=None) -> int:
+    """Status word of the last call on the model's workspace (0: every wait
+    of that call ended as it should); synchronises the stream."""
+    import torch
+
+    out = torch.empty(1, dtype=torch.int32, device=model.ws.device)
+    mv_step_status(model.ws, out, stream)
+    return int(out.cpu()[0])
 
 
 def to_device(arr: np.ndarray, device: str = "cuda"):

@@ -2,6 +2,7 @@
 // carving and the launch sequence on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -15,6 +16,8 @@
 namespace {
 
 thread_local std::string g_err;
+// Polls a fused-launch wait makes before it gives up (mv_set_spin_limit).
+std::atomic<int> g_spin_limit{mv::kSpinLimitDefault};
 
 int fail(int code, const char *msg) {
   g_err = msg;
@@ -56,7 +59,7 @@ int max_tiles(const mv_config &c, int T, int tm) {
 int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T)); }
 
 struct Layout {
-  size_t hbuf, hbuf2, hbuf3, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, logits, tdone,
+  size_t status, hbuf, hbuf2, hbuf3, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, logits, tdone,
       total;
 };
 
@@ -77,6 +80,8 @@ Layout layout(const mv_config &c, int T) {
     off += align256(bytes);
     return at;
   };
+  // the call's status word, at offset 0 whatever T is (mv_step_status)
+  L.status = take(4);
   L.hbuf = take(static_cast<size_t>(T) * c.d_model * es);
   // the combines of a verify step alternate between hidden-state buffers
   L.hbuf2 = take(static_cast<size_t>(T) * c.d_model * es);
@@ -95,8 +100,8 @@ Layout layout(const mv_config &c, int T) {
   L.done = take(4);
   L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
   L.logits = take(static_cast<size_t>(T) * 64 * 4);
-  // two sets of fused-launch counters (tiles, then the routing copies), then the timeout word
-  L.tdone = take((2 * done_set_words(c, T) + mv::kDoneStride) * 4);
+  // two sets of fused-launch counters (tiles, then the routing copies)
+  L.tdone = take(2 * done_set_words(c, T) * 4);
   L.total = off;
   return L;
 }
@@ -219,7 +224,7 @@ struct Step {
     return reinterpret_cast<unsigned *>(ws + L.tdone) + static_cast<size_t>(s) * done_set_words(c, T);
   }
   int done_count() const { return max_tiles(c, T, mv::kTileM) + mv::kRouteCopies; }
-  unsigned *done_err() const { return done_set(2); }
+  unsigned *status() const { return reinterpret_cast<unsigned *>(ws + L.status); }
   // LDS-tiled GEMMs; the combine is in the shared experts' down projection
   bool gemm() const { return path_for(c, T) == kGemmTiles; }
 
@@ -227,9 +232,11 @@ struct Step {
   // With `slots`, h_dst = h_src + the previous layer's expert outputs first.
   // `logits`: routing stops at the logits (mode kRoute only; the ffn of the
   // same layer then takes the top-k).
+  // `first`: the call's first launch, which clears its status word.
   int route(int layer, int mode, const void *h_src, void *h_dst, const float *slots_in,
-            float *y_moe, int *ids, float *gates_out, bool logits = false) const {
+            float *y_moe, int *ids, float *gates_out, bool logits = false, bool first = false) const {
     mv::RouteArgs a = route_args(layer, mode, ids, gates_out);
+    if (first) a.status = status();
     if (logits && mode == mv::kRoute) {  // also clears counter set 0 for the first fused launch
       a.mode = mv::kLogits;
       a.logits = this->logits();
@@ -291,7 +298,8 @@ struct Step {
       e.route_done = done_set(set) + static_cast<size_t>(max_tiles(c, T, mv::kTileM)) * mv::kDoneStride;
       e.done_next = done_set(1 - set);
       e.n_done = done_count();
-      e.err = done_err();
+      e.err = status();
+      e.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
       e.w_routed_down = lp.down;
       e.w_shared_down = lp.sdown;
       return hip_status(mv::launch_ffn_small(c.dtype, e, ra, ca, mt, s));
@@ -340,7 +348,7 @@ MV_API int moe_layer_forward(const mv_config *cfg, const mv_weights *w, int32_t 
   Step st{*cfg, *w, T, static_cast<char *>(ws), layout(*cfg, T), static_cast<hipStream_t>(stream)};
   int *ids = topk_ids ? topk_ids : reinterpret_cast<int *>(st.ws + st.L.ids);
   float *gates = topk_w ? topk_w : st.gates();
-  if ((rc = st.route(layer, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates))) return rc;
+  if ((rc = st.route(layer, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, false, true))) return rc;
   if (st.gemm()) return st.ffn(layer, ids, gates, h_in, h_out, y_moe);
   if ((rc = st.ffn(layer, ids, gates))) return rc;
   return st.route(layer, mv::kCombine, h_in, h_out, st.slots(), y_moe, nullptr, nullptr);
@@ -377,7 +385,7 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
                             : reinterpret_cast<int *>(st.ws + st.L.ids);
     const void *src = layer == 0 ? h_in : hbuf;
     if (gemm) {  // the layer's own combine writes hbuf
-      if ((rc = st.route(layer, mv::kRoute, src, nullptr, nullptr, nullptr, ids, gates)) ||
+      if ((rc = st.route(layer, mv::kRoute, src, nullptr, nullptr, nullptr, ids, gates, false, layer == 0)) ||
           (rc = st.ffn(layer, ids, gates, src, hbuf)))
         return rc;
       continue;
@@ -390,7 +398,7 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
     // fused expert launch.
     const bool lg = st.logits_route();
     if (layer == 0) {
-      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, lg);
+      rc = st.route(0, mv::kRoute, h_in, nullptr, nullptr, nullptr, ids, gates, lg, true);
       if (rc || (rc = st.ffn(0, ids, gates, nullptr, nullptr, nullptr, lg))) return rc;
       continue;
     }
@@ -607,6 +615,19 @@ MV_API double mv_step_bytes(const mv_config *cfg, int32_t B, int32_t K, int32_t 
   bytes += 2.0 * T * d * es;                                         // rows in and out
   bytes += K * ((2.0 * d * d + 3.0 * d_ff_mtp * d + V * d + 4.0 * d) * es + B * 3.0 * d * es);  // draft block
   return bytes;
+}
+
+MV_API int mv_step_status(const void *ws, int32_t *status, void *stream) {
+  g_err.clear();
+  if (!ws || !status) return fail(MV_ERR_NULL, "ws and status are required");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  // the status word sits at offset 0 of every layout
+  const unsigned *word = static_cast<const unsigned *>(ws);
+  return hip_status(mv::launch_copy_status(word, status, static_cast<hipStream_t>(stream)));
+}
+
+MV_API int32_t mv_set_spin_limit(int32_t polls) {
+  return g_spin_limit.exchange(polls < 0 ? mv::kSpinLimitDefault : polls);
 }
 
 MV_API const char *mv_last_error(void) { return g_err.c_str(); }

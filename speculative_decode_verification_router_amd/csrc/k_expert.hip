@@ -199,17 +199,21 @@ __global__ __launch_bounds__(kThreads) void k_down(ExpertArgs p) {
 // stores and, once they have completed, counts itself on its tile's counter.
 // A down block waits, without requesting anything else, until every gate/up
 // block of its tile has counted; then it requests its weights and reads the
-// products with agent-scope loads.  A down block only waits for blocks of lower index, dispatched
-// before it; the wait is bounded, and a timeout is recorded in *err.
-constexpr int kSpinLimit = 1 << 18;  // polls of about a microsecond each
+// products with agent-scope loads.  Every wait is for blocks of lower index
+// (routing blocks, then gate/up blocks), which in-order dispatch places on
+// the chip before the waiter, so with every waiter also resident the waits
+// end.  Should a launch be starved (say, preempted), the waits are bounded:
+// the result of that call is then wrong, and its status word says so.
 
-// Thread 0 waits (bounded) until *ctr >= target; a timeout is recorded in
-// *err.  The caller synchronises the block afterwards.
-__device__ __forceinline__ void wait_count(const unsigned *ctr, unsigned target, unsigned *err) {
+// Thread 0 waits until *ctr >= target, for at most `limit` polls (about a
+// microsecond each); a wait that gives up records 1 in *err (the call's
+// status word, read back with mv_step_status) and the block goes on.  The
+// caller synchronises the block afterwards.
+__device__ __forceinline__ void wait_count(const unsigned *ctr, unsigned target, unsigned *err, int limit) {
   if (threadIdx.x != 0) return;
   unsigned n = 0;
   int polls = 0;
-  while ((n = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target && ++polls < kSpinLimit)
+  while ((n = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target && polls++ < limit)
     __builtin_amdgcn_s_sleep(64);
   if (n < target) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   } else {
     if (n_route) {
-      wait_count(route_ctr, n_route, p.err);
+      wait_count(route_ctr, n_route, p.err, p.spin_limit);
       __syncthreads();
     }
     const bool record = gu && y == n_sh && pair == 0;  // writes ids and gates of record
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs 
     GateUpPart<T, kUnrollFused> part;
     part.begin(p, ti, pair, tid);
     if (shared && n_route) {  // x is written by this launch's routing blocks
-      wait_count(route_ctr, n_route, p.err);
+      wait_count(route_ctr, n_route, p.err, p.spin_limit);
       __syncthreads();
     }
     const int nvec = d / VN, lda = d + VN;
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs 
   }
 
   // no weight requests before the tile is ready: the wait takes no bandwidth
-  wait_count(p.tile_done + y * kDoneStride, static_cast<unsigned>(sp_gu), p.err);
+  wait_count(p.tile_done + y * kDoneStride, static_cast<unsigned>(sp_gu), p.err, p.spin_limit);
   __syncthreads();
   DownPart<T, kUnrollFused> part;
   part.begin(p, ti, pair, tid, p.w_routed_down, p.w_shared_down);

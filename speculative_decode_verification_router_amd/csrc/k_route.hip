@@ -102,7 +102,16 @@ __global__ __launch_bounds__(256) void k_permute_large(RouteArgs p) {
   }
 }
 
+__global__ void k_copy_status(const unsigned *word, int32_t *status) {
+  status[0] = static_cast<int32_t>(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 }  // namespace
+
+hipError_t launch_copy_status(const unsigned *word, int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_status, dim3(1), dim3(1), 0, s, word, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int ntok, hipStream_t s) {
   const size_t smem = route_smem(ntok, a.d, dtype == 1 ? 2 : 4).total;

@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
   const int t0 = blockIdx.x * kRLTok, nt = min(kRLTok, a.T - t0);
 
   if (tid < 64) cnt[tid] = 0;
+  if (a.status && blockIdx.x == 0 && tid == 0) *a.status = 0u;  // first launch of a call
   // router weights first: wavefront w takes experts 32*(w&1) .. +31 over K
   // quarter w>>1, its fragments requested before the rows are read
   const int nwin = d / 16, quarter = wv >> 1;

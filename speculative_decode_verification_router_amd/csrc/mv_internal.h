@@ -44,6 +44,9 @@ constexpr int kDoneStride = 64;
 // Copies of the routing counter of a fused launch that also routes, so that
 // its many waiting blocks spread their polls over that many lines.
 constexpr int kRouteCopies = 32;
+// Polls (about a microsecond each) a fused-launch wait makes before it gives
+// up and records the timeout in the call's status word.
+constexpr int kSpinLimitDefault = 1 << 18;
 
 struct RouteArgs {
   int T, d, E, S, k, nslot, mode;
@@ -62,6 +65,7 @@ struct RouteArgs {
   float *logits;            // kLogits: [T, 64] fp32 router logits
   unsigned *tile_done;      // kLogits: counters [i * kDoneStride], i < n_tile_done, cleared for the fused expert launch
   int n_tile_done;
+  unsigned *status;         // if set: block 0 clears the call's status word (first launch of a call)
 };
 
 // Combine of the previous layer's expert slots into the hidden state.
@@ -98,7 +102,8 @@ struct ExpertArgs {
   unsigned *route_done;    // [copy * kDoneStride]: routing blocks done, kRouteCopies copies
   unsigned *done_next;     // [i * kDoneStride], i < n_done
   int n_done;
-  unsigned *err;           // set to 1 if a fused launch's wait timed out
+  unsigned *err;           // the call's status word: set to 1 if a fused launch's wait gave up
+  int spin_limit;          // polls before a fused launch's wait gives up
 };
 
 struct AcceptArgs {
@@ -170,5 +175,7 @@ int route_large_blocks(int T);
 hipError_t launch_route_large(const RouteArgs &a, const void *h, int *blk_cnt, hipStream_t s);
 hipError_t launch_lm_argmax(int dtype, const LmArgs &a, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t s);
+// status[0] = *word (int32), one thread.
+hipError_t launch_copy_status(const unsigned *word, int32_t *status, hipStream_t s);
 
 }  // namespace mv

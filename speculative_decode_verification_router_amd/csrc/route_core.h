@@ -172,6 +172,7 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
   const bool writer = eg == 0;                                           // h_dst and x_out
   if (logits_only && blockIdx.x == 0)
     for (int i = tid; i < a.n_tile_done; i += blockDim.x) a.tile_done[i * kDoneStride] = 0u;
+  if (a.status && blockIdx.x == 0 && tid == 0) *a.status = 0u;  // first launch of a call
   uint4 wq[kRouterChunks];
   if ((a.mode == kRoute || logits_only) && router_wave)
     router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, e_blk + 4 * wv, d);

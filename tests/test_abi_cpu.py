@@ -189,3 +189,29 @@ def test_mtp_draft_zero_work_is_a_no_op(lib):
                   ws=None) == bd.MV_OK
     assert _draft(lib, _cfg(), _weights(), _mtp(), K=0, h_in=None, tokens=None, drafts=None,
                   ws=None) == bd.MV_OK
+
+
+# ---------------------------------------------------------------- call status
+
+
+def test_step_status_rejects_bad_arguments(lib):
+    assert lib.mv_step_status(None, FAKE, None) == bd.MV_ERR_NULL
+    assert lib.mv_step_status(FAKE, None, None) == bd.MV_ERR_NULL
+    assert lib.mv_step_status(FAKE + 8, FAKE, None) == bd.MV_ERR_WORKSPACE
+    assert bd.mv_last_error() != ""
+
+
+def test_spin_limit_hook_round_trip(lib):
+    default = 1 << 18
+    assert bd.mv_set_spin_limit(5) == default
+    assert bd.mv_set_spin_limit(0) == 5
+    assert bd.mv_set_spin_limit(-1) == 0
+    assert bd.mv_set_spin_limit(-1) == default
+
+
+def test_status_word_sits_before_every_region(lib):
+    """The status word is at offset 0 whatever the call's T: a workspace
+    sized for T rows is larger than one sized for fewer rows by whole
+    regions, never by a shift of the status word (it is the first region)."""
+    c = _cfg()
+    assert bd.mv_workspace_bytes(c, 0) >= 256

@@ -144,6 +144,7 @@ def test_draft_verify_accept_loop_is_lossless(bd, torch_cuda, tiny):
         rows = np.stack([emb[c]] + [emb[int(t)] for t in bd.to_host(drafts)[0]])
         out = bd.run_verify_step(model, bd.to_device(rows), drafts, 1, K)
         torch_cuda.cuda.synchronize()
+        assert bd.step_status(model) == 0      # every wait of the fused launches ended
         k = int(bd.to_host(out["n_committed"])[0])
         accepted += k - 1
         seq.extend(int(t) for t in bd.to_host(out["committed"])[0, :k])

@@ -26,18 +26,41 @@ def bd(gpu_lib):
     return binding
 
 
+_MODELS = []  # every DeviceModel of this module, for the status check after each test
+
+
+def _model(bd, dims, W, max_tokens):
+    m = bd.DeviceModel(dims, W, max_tokens=max_tokens)
+    m.ws[:256].zero_()  # a status word no call has written yet reads 0
+    _MODELS.append(m)
+    return m
+
+
+@pytest.fixture(autouse=True)
+def _calls_completed(request):
+    """After every test: the last call on each workspace ended every bounded
+    wait of its fused launches as it should (mv_step_status = 0)."""
+    yield
+    if "bd" not in request.fixturenames:
+        return
+    from speculative_decode_verification_router_amd import binding
+
+    for m in _MODELS:
+        assert binding.step_status(m) == 0, "a fused launch's wait gave up"
+
+
 @pytest.fixture(scope="module")
 def tiny(bd):
     dims = synth.TINY_F32
     W = synth.make_weights(dims, seed=0, gamma="uniform")
-    return dims, W, bd.DeviceModel(dims, W, max_tokens=512)
+    return dims, W, _model(bd, dims, W, 512)
 
 
 @pytest.fixture(scope="module")
 def big(bd):
     dims = synth.DS3B_BF16
     W = synth.make_weights(dims, seed=0, sigma=0.02)
-    return dims, W, bd.DeviceModel(dims, W, max_tokens=10048)
+    return dims, W, _model(bd, dims, W, 10048)
 
 
 @pytest.fixture(scope="module")
@@ -48,7 +71,7 @@ def tiny3(bd):
 
     dims = dataclasses.replace(synth.TINY_F32, n_layers=3)
     W = synth.make_weights(dims, seed=4, gamma="uniform")
-    return dims, W, bd.DeviceModel(dims, W, max_tokens=64)
+    return dims, W, _model(bd, dims, W, 64)
 
 
 def _dev(bd, a):
@@ -476,3 +499,36 @@ def test_verify_step_in_a_graph(bd, torch_cuda, big, B, K):
         _sync(torch)
         for key, want in ref.items():
             assert np.array_equal(_host(bd, out[key]), want), (rep, key)
+
+
+# ---------------------------------------------------------------- bounded waits
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_wait_timeout_is_reported(bd, torch_cuda, big, B):
+    """The fused launch's waits are bounded.  With the bound set to zero polls
+    from the host, waits that find their counters short give up at once, the
+    kernels still run to their end, and the call's status word reads 1; the
+    next call with the default bound clears it and reads 0 again, with the
+    same results as before the forced timeout."""
+    torch = torch_cuda
+    dims, W, model = big
+    K = 3
+    h = _dev(bd, synth.make_hidden(dims, B * (K + 1), seed=830 + B))
+    drafts = _dev(bd, np.zeros((B, K), np.int32))
+    ref = bd.run_verify_step(model, h, drafts, B, K, routing=True)
+    _sync(torch)
+    assert bd.step_status(model) == 0
+    prev = bd.mv_set_spin_limit(0)
+    try:
+        bd.run_verify_step(model, h, drafts, B, K, routing=True)
+        _sync(torch)
+        forced = bd.step_status(model)
+    finally:
+        bd.mv_set_spin_limit(prev)
+    assert forced == 1
+    again = bd.run_verify_step(model, h, drafts, B, K, routing=True)
+    _sync(torch)
+    assert bd.step_status(model) == 0
+    for key in ("h_out", "argmax", "topk_ids"):
+        assert np.array_equal(_host(bd, again[key]), _host(bd, ref[key])), key
