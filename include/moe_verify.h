@@ -142,6 +142,25 @@ int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
                     int32_t *dbg_topk_ids, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* moe_verify_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments and results as in moe_verify_step, without ws and ws_bytes: the
+ * workspace is a static 16 MiB array of the library, one per GPU, looked up
+ * (not allocated) on the first call on that GPU and held until the process
+ * ends.  The call allocates nothing.  Steps whose workspace
+ * (mv_workspace_bytes(cfg, B*(K+1))) exceeds 16 MiB are rejected with
+ * MV_ERR_WORKSPACE: about 250 rows at d_model 1280, d_ff 896, 64 + 2
+ * experts, top-6 (B = 32, K = 3 takes 8.1 MiB).  Every call on one GPU uses
+ * the same array and leaves its contents behind; the kernels clear what must
+ * start at zero, so consecutive calls are independent, but two calls that
+ * overlap on one GPU (other streams, other threads) race.  mv_step_status
+ * with ws = NULL reads this array's status word. */
+int moe_verify_step_noalloc(const mv_config *cfg, const mv_weights *w, int32_t B,
+                            int32_t K, const void *h_in, const int32_t *drafts,
+                            void *h_out, int32_t *argmax, int32_t *n_accepted,
+                            int32_t *committed, int32_t *n_committed,
+                            int32_t *dbg_topk_ids, void *stream);
+
 /* The accept rule alone (FastMTP paragraph of the ainewsfeed page), on
  * argmax [B, K+1] and drafts [B, K]; outputs as in moe_verify_step.
  * Limits: 0 <= K <= 15.  No workspace. */
@@ -233,8 +252,9 @@ double mv_step_bytes(const mv_config *cfg, int32_t B, int32_t K, int32_t d_ff_mt
  * word at offset 0 of the workspace, which the first launch of every call
  * clears.  This call enqueues, on `stream`, a copy of that word into
  * status[0] (device memory, int32): 0 means every wait of the call ended as
- * it should; 1 means the call's results must not be used.  Errors:
- * MV_ERR_NULL, MV_ERR_WORKSPACE (ws not 256-byte aligned). */
+ * it should; 1 means the call's results must not be used.  ws = NULL reads
+ * the current GPU's static workspace of moe_verify_step_noalloc.  Errors:
+ * MV_ERR_NULL (status NULL), MV_ERR_WORKSPACE (ws not 256-byte aligned). */
 int mv_step_status(const void *ws, int32_t *status, void *stream);
 
 /* Test hook for the bounded waits above: the number of polls (each about a

@@ -19,7 +19,8 @@ from .build import LIB_PATH
 MV_F32, MV_BF16 = 0, 1
 MV_OK, MV_ERR_NULL, MV_ERR_SHAPE, MV_ERR_UNSUPPORTED, MV_ERR_WORKSPACE, MV_ERR_HIP = 0, -1, -2, -3, -4, -5
 
-EXPORTED = ("mv_workspace_bytes", "moe_layer_forward", "moe_verify_step", "spec_accept",
+EXPORTED = ("mv_workspace_bytes", "moe_layer_forward", "moe_verify_step", "moe_verify_step_noalloc",
+            "spec_accept",
             "mtp_workspace_bytes", "mtp_draft", "mv_choose_k", "mv_step_bytes", "mv_step_status",
             "mv_set_spin_limit", "mv_last_error")
 
@@ -67,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_layer_forward.restype = ctypes.c_int
     lib.moe_verify_step.argtypes = [cfgp, wp, I, I, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_verify_step.restype = ctypes.c_int
+    lib.moe_verify_step_noalloc.argtypes = [cfgp, wp, I, I, P, P, P, P, P, P, P, P, P]
+    lib.moe_verify_step_noalloc.restype = ctypes.c_int
     lib.spec_accept.argtypes = [I, I, P, P, P, P, P, P]
     lib.spec_accept.restype = ctypes.c_int
     mwp = ctypes.POINTER(MtpWeights)
@@ -148,6 +151,15 @@ def moe_verify_step(cfg: MvConfig, weights: MvWeights, B: int, K: int, h_in, dra
                                   _ptr(drafts), _ptr(h_out), _ptr(argmax), _ptr(n_accepted),
                                   _ptr(committed), _ptr(n_committed), _ptr(dbg_topk_ids),
                                   _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_verify_step_noalloc(cfg: MvConfig, weights: MvWeights, B: int, K: int, h_in, drafts, h_out,
+                            argmax, n_accepted, committed, n_committed, dbg_topk_ids=None,
+                            stream=None) -> None:
+    _check(load().moe_verify_step_noalloc(ctypes.byref(cfg), ctypes.byref(weights), B, K, _ptr(h_in),
+                                          _ptr(drafts), _ptr(h_out), _ptr(argmax), _ptr(n_accepted),
+                                          _ptr(committed), _ptr(n_committed), _ptr(dbg_topk_ids),
+                                          _stream(stream)))
 
 
 def spec_accept(B: int, K: int, argmax, drafts, n_accepted, committed, n_committed,

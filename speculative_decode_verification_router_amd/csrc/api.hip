@@ -6,12 +6,20 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "moe_verify.h"
 #include "mv_internal.h"
 
 #define MV_API extern "C" __attribute__((visibility("default")))
+
+// Workspace of moe_verify_step_noalloc: one array per GPU, loaded with the
+// library's code object and held until the process ends.  In host code the
+// name stands for a host-side symbol, not a device address: the address of
+// each device's copy comes from hipGetSymbolAddress (scratch_on_device).
+constexpr size_t kScratchBytes = static_cast<size_t>(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -354,11 +362,13 @@ MV_API int moe_layer_forward(const mv_config *cfg, const mv_weights *w, int32_t 
   return st.route(layer, mv::kCombine, h_in, h_out, st.slots(), y_moe, nullptr, nullptr);
 }
 
-MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
-                           const void *h_in, const int32_t *drafts, void *h_out, int32_t *argmax,
-                           int32_t *n_accepted, int32_t *committed, int32_t *n_committed,
-                           int32_t *dbg_topk_ids, void *ws, size_t ws_bytes, void *stream) {
-  g_err.clear();
+namespace {
+
+// Arguments of a verify step other than the workspace; B > 0 means there is
+// work (the workspace is checked next).
+int check_verify(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K, const void *h_in,
+                 const int32_t *drafts, const int32_t *argmax, const int32_t *n_accepted, const int32_t *committed,
+                 const int32_t *n_committed) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (B < 0 || K < 0) return fail(MV_ERR_SHAPE, "B and K must be >= 0");
@@ -368,12 +378,18 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
   if ((rc = check_layer_weights(cfg, w))) return rc;
   if (!w->final_norm || !w->lm_head) return fail(MV_ERR_NULL, "final_norm and lm_head are required");
   if (B == 0) return MV_OK;
-  const int T = static_cast<int>(Tl);
   if (!h_in || !argmax || !n_accepted || !committed || !n_committed)
     return fail(MV_ERR_NULL, "h_in, argmax, n_accepted, committed and n_committed are required");
   if (K > 0 && !drafts) return fail(MV_ERR_NULL, "drafts is required when K > 0");
-  if ((rc = check_ws(cfg, T, ws, ws_bytes))) return rc;
+  return MV_OK;
+}
 
+// The verify step's launch sequence, arguments and workspace already checked.
+int verify_launches(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K, const void *h_in,
+                    const int32_t *drafts, void *h_out, int32_t *argmax, int32_t *n_accepted, int32_t *committed,
+                    int32_t *n_committed, int32_t *dbg_topk_ids, void *ws, void *stream) {
+  int rc = MV_OK;
+  const int T = B * (K + 1);
   Step st{*cfg, *w, T, static_cast<char *>(ws), layout(*cfg, T), static_cast<hipStream_t>(stream)};
   void *hbuf = h_out ? h_out : static_cast<void *>(st.ws + st.L.hbuf);
   const int L = cfg->n_layers, k = cfg->top_k;
@@ -426,6 +442,61 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
   const mv::AcceptArgs aa{B, K, st.argkey(), nullptr, argmax, drafts, n_accepted, committed, n_committed};
   const mv::LmArgs la{T, cfg->d_model, cfg->vocab, st.ws + st.L.x, w->lm_head, st.argkey(), st.done(), aa};
   return hip_status(mv::launch_lm_argmax(cfg->dtype, la, st.s));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first use on that device, with that device current).
+int scratch_on_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(MV_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_err = std::string("hipGetSymbolAddress of the static scratch failed: ") + hipGetErrorString(e);
+      return MV_ERR_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MV_OK;
+}
+
+}  // namespace
+
+MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
+                           const void *h_in, const int32_t *drafts, void *h_out, int32_t *argmax,
+                           int32_t *n_accepted, int32_t *committed, int32_t *n_committed,
+                           int32_t *dbg_topk_ids, void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  int rc = check_verify(cfg, w, B, K, h_in, drafts, argmax, n_accepted, committed, n_committed);
+  if (rc || B == 0) return rc;
+  if ((rc = check_ws(cfg, B * (K + 1), ws, ws_bytes))) return rc;
+  return verify_launches(cfg, w, B, K, h_in, drafts, h_out, argmax, n_accepted, committed, n_committed,
+                         dbg_topk_ids, ws, stream);
+}
+
+MV_API int moe_verify_step_noalloc(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
+                                   const void *h_in, const int32_t *drafts, void *h_out, int32_t *argmax,
+                                   int32_t *n_accepted, int32_t *committed, int32_t *n_committed,
+                                   int32_t *dbg_topk_ids, void *stream) {
+  g_err.clear();
+  int rc = check_verify(cfg, w, B, K, h_in, drafts, argmax, n_accepted, committed, n_committed);
+  if (rc || B == 0) return rc;
+  if (layout(*cfg, B * (K + 1)).total > kScratchBytes)
+    return fail(MV_ERR_WORKSPACE, "this step needs more than the 16 MiB static scratch of moe_verify_step_noalloc "
+                                  "(mv_workspace_bytes(cfg, B*(K+1)) > 16 MiB); use moe_verify_step");
+  void *ws = nullptr;
+  if ((rc = scratch_on_device(&ws))) return rc;
+  return verify_launches(cfg, w, B, K, h_in, drafts, h_out, argmax, n_accepted, committed, n_committed,
+                         dbg_topk_ids, ws, stream);
 }
 
 MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_t *drafts,
@@ -619,7 +690,13 @@ MV_API double mv_step_bytes(const mv_config *cfg, int32_t B, int32_t K, int32_t 
 
 MV_API int mv_step_status(const void *ws, int32_t *status, void *stream) {
   g_err.clear();
-  if (!ws || !status) return fail(MV_ERR_NULL, "ws and status are required");
+  if (!status) return fail(MV_ERR_NULL, "status is required");
+  if (!ws) {  // the current device's static scratch (moe_verify_step_noalloc)
+    void *p = nullptr;
+    const int rc = scratch_on_device(&p);
+    if (rc) return rc;
+    ws = p;
+  }
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   // the status word sits at offset 0 of every layout
   const unsigned *word = static_cast<const unsigned *>(ws);

@@ -195,7 +195,6 @@ def test_mtp_draft_zero_work_is_a_no_op(lib):
 
 
 def test_step_status_rejects_bad_arguments(lib):
-    assert lib.mv_step_status(None, FAKE, None) == bd.MV_ERR_NULL
     assert lib.mv_step_status(FAKE, None, None) == bd.MV_ERR_NULL
     assert lib.mv_step_status(FAKE + 8, FAKE, None) == bd.MV_ERR_WORKSPACE
     assert bd.mv_last_error() != ""
@@ -215,3 +214,22 @@ def test_status_word_sits_before_every_region(lib):
     regions, never by a shift of the status word (it is the first region)."""
     c = _cfg()
     assert bd.mv_workspace_bytes(c, 0) >= 256
+
+
+def test_noalloc_verify_step_rejects_bad_arguments(lib):
+    """Validation happens before the static scratch is looked up: none of
+    these touches a device."""
+    cfg, w = _cfg(), _weights()
+
+    def call(B=1, K=3, h_in=FAKE, argmax=FAKE, c=cfg, ww=w):
+        return lib.moe_verify_step_noalloc(ctypes.byref(c), ctypes.byref(ww), B, K, h_in, FAKE, None, argmax,
+                                           FAKE, FAKE, FAKE, None, None)
+    assert call(h_in=None) == bd.MV_ERR_NULL
+    assert call(argmax=None) == bd.MV_ERR_NULL
+    assert call(K=16) == bd.MV_ERR_SHAPE
+    assert call(c=_cfg(dtype=3)) == bd.MV_ERR_UNSUPPORTED
+    # 64 sequences x 4 rows need 16.2 MiB of workspace, above the 16 MiB array
+    assert bd.mv_workspace_bytes(cfg, 256) > 16 << 20 >= bd.mv_workspace_bytes(cfg, 128)
+    assert call(B=64) == bd.MV_ERR_WORKSPACE
+    assert "16 MiB" in bd.mv_last_error()
+    assert call(B=0, h_in=None, argmax=None) == bd.MV_OK

@@ -1,0 +1,81 @@
+"""moe_verify_step_noalloc (static per-GPU scratch) against moe_verify_step
+(caller's workspace), through the C ABI: two calls in a row, the second on a
+smaller batch, must give bit-identical results (the same kernels on the same
+inputs), and a step larger than the static scratch is refused."""
+import numpy as np
+import pytest
+
+from speculative_decode_verification_router_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("h_out", "argmax", "n_accepted", "committed", "n_committed", "topk_ids")
+
+
+@pytest.fixture(scope="module")
+def bd(gpu_lib):
+    from speculative_decode_verification_router_amd import binding
+
+    return binding
+
+
+def _noalloc(bd, model, h, drafts, B, K):
+    import torch
+
+    T = B * (K + 1)
+    out = dict(argmax=torch.full((T,), -9, dtype=torch.int32, device="cuda"),
+               n_accepted=torch.full((B,), -9, dtype=torch.int32, device="cuda"),
+               committed=torch.full((B, K + 1), -9, dtype=torch.int32, device="cuda"),
+               n_committed=torch.full((B,), -9, dtype=torch.int32, device="cuda"),
+               h_out=torch.zeros_like(h),
+               topk_ids=torch.full((model.dims.n_layers, T, model.dims.top_k), -9, dtype=torch.int32,
+                                   device="cuda"))
+    bd.moe_verify_step_noalloc(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
+                               out["n_accepted"], out["committed"], out["n_committed"], out["topk_ids"])
+    return out
+
+
+def _status_noalloc(bd):
+    import torch
+
+    s = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    bd.mv_step_status(None, s)
+    return int(s.cpu()[0])
+
+
+def _compare(bd, model, dims, calls, seed):
+    import torch
+
+    rng = np.random.default_rng(seed)
+    for i, (B, K) in enumerate(calls):
+        T = B * (K + 1)
+        print(f"no-alloc call {i}: B={B} K={K} T={T}", flush=True)
+        h = bd.to_device(synth.make_hidden(dims, T, seed=seed + i))
+        drafts = bd.to_device(rng.integers(0, dims.vocab, (B, K)).astype(np.int32))
+        ref = bd.run_verify_step(model, h, drafts, B, K, routing=True)
+        got = _noalloc(bd, model, h, drafts, B, K)
+        torch.cuda.synchronize()
+        for key in KEYS:
+            assert np.array_equal(bd.to_host(got[key]), bd.to_host(ref[key])), (i, key)
+        assert _status_noalloc(bd) == 0
+
+
+def test_noalloc_matches_workspace_call_tiny(bd):
+    dims = synth.TINY_F32
+    W = synth.make_weights(dims, seed=0, gamma="uniform")
+    model = bd.DeviceModel(dims, W, max_tokens=64)
+    _compare(bd, model, dims, [(7, 3), (2, 1)], seed=900)
+
+
+def test_noalloc_matches_workspace_call_full_width(bd):
+    dims = synth.DS3B_BF16
+    W = synth.make_weights(dims, seed=0, sigma=0.02)
+    model = bd.DeviceModel(dims, W, max_tokens=128)
+    # 128 rows (16-row tiles, separate launches), then 4 rows (fused launches)
+    _compare(bd, model, dims, [(32, 3), (1, 3)], seed=910)
+    # a step above the static scratch is refused before anything is enqueued
+    B, K = 64, 3
+    with pytest.raises(bd.MvError) as e:
+        _noalloc(bd, model, bd.to_device(synth.make_hidden(dims, B * (K + 1), seed=7)),
+                 bd.to_device(np.zeros((B, K), np.int32)), B, K)
+    assert e.value.code == bd.MV_ERR_WORKSPACE
