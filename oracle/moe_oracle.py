@@ -49,7 +49,10 @@ before the LM head.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 and tests/test_mtp_pins.py (library special cases, closed forms, invariants,
-brute force, and the lossless greedy-equivalence property).
+brute force, and the lossless greedy-equivalence property).  The loop over
+layers (forward_tokens) is pinned on a three-layer model: zero down
+projections give the identity, and per-layer one-hot router biases give the
+chain of the chosen experts' dense FFNs computed with torch.
 """
 from __future__ import annotations
 

@@ -384,3 +384,133 @@ def test_lossless_pin_catches_commit_past_first_mismatch():
         greedy.append(int(table[greedy[-1]]))
     spec, _ = _spec_decode(dims, W, emb, 17, 60, K=3, p=0.6, seed=3, accept=one_too_many)
     assert spec != greedy[1:]
+
+
+# ---------------------------------------------------------------- the layer stack
+
+
+def _stack_weights(dtype="f32", layers=3, seed=11):
+    import dataclasses
+
+    dims = dataclasses.replace(synth.TINY_F32, n_layers=layers, dtype=dtype)
+    return dims, synth.make_weights(dims, seed=seed, gamma="uniform")
+
+
+def test_stack_with_zero_down_projections_is_the_identity():
+    """Every expert's down projection zero in every layer: each layer adds an
+    exact zero, so the stack returns its input bit for bit (a loop that
+    carried x, or anything but h, from layer to layer would not)."""
+    for dtype in ("f32", "bf16"):
+        dims, W = _stack_weights(dtype)
+        W["w_down"][...] = 0
+        W["ws_down"][...] = 0
+        h = synth.make_hidden(dims, 7, seed=12)
+        out = O.forward_tokens(h, W, dims, lm_head=False)
+        assert np.array_equal(out["h_out"], O.widen(h, dtype))
+        assert len(out["layers"]) == dims.n_layers
+
+
+def _one_hot_chain(dims, W, e_star):
+    """Router bias +1e4 on expert e_star[l] and -1e4 elsewhere in layer l."""
+    b = np.full((dims.n_layers, dims.n_routed), -1e4, np.float32)
+    for layer, e in enumerate(e_star):
+        b[layer, e] = 1e4
+    W = dict(W)
+    W["router_b"] = b
+    return W
+
+
+def _torch_chain(dims, W, h, e_star):
+    """h <- h + FFN_{e*_l}(x) + FFN_shared0(x) + FFN_shared1(x), x = RMSNorm(h) * gamma_l,
+    layer by layer, in float64 torch with no intermediate rounding."""
+    wid = lambda a: O.widen(a, dims.dtype)
+    ht = torch.from_numpy(O.widen(h, dims.dtype))
+    for layer, e in enumerate(e_star):
+        g = torch.from_numpy(wid(W["ffn_norm"][layer]))
+        x = torch.nn.functional.rms_norm(ht, (dims.d_model,), g, eps=dims.rms_eps).numpy()
+        y = _torch_ffn(x, wid(W["w_gate_up"][layer, e]), wid(W["w_down"][layer, e]))
+        for s in range(dims.n_shared):
+            y = y + _torch_ffn(x, wid(W["ws_gate_up"][layer, s]), wid(W["ws_down"][layer, s]))
+        ht = ht + torch.from_numpy(y)
+    return ht.numpy()
+
+
+E_STAR = (37, 5, 62)
+
+
+def _chain_agrees(forward=O.forward_tokens):
+    dims, W = _stack_weights("f32")
+    W = _one_hot_chain(dims, W, E_STAR)
+    h = synth.make_hidden(dims, 6, seed=13)
+    out = forward(h, W, dims, lm_head=False)
+    ids_ok = all(np.all(out["layers"][layer]["ids"][:, 0] == e) for layer, e in enumerate(E_STAR))
+    ref = _torch_chain(dims, W, h, E_STAR)
+    err = np.abs(out["h_out"] - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    # fp32 storage of x, a and h in three layers against float64 without rounding
+    return ids_ok and bool(np.all(err < 1e-5)), float(err.max())
+
+
+def test_stack_with_one_hot_routers_chains_the_dense_ffns():
+    """Per-layer one-hot router biases with a different expert in every layer:
+    the stack is the chain of those experts' dense SwiGLU FFNs plus the shared
+    ones, each behind its own layer's RMSNorm, compared with torch."""
+    ok, err = _chain_agrees()
+    assert ok, err
+
+
+def test_chain_pin_catches_a_wrong_layer_index(monkeypatch):
+    """Planted mistake (in the oracle, on the CPU): every layer of the stack
+    reads layer 0's weights.  The chain pin fails."""
+    real = O.moe_layer
+    monkeypatch.setattr(O, "moe_layer", lambda h, W, layer, dims, ftype=np.float64: real(h, W, 0, dims, ftype))
+    ok, _ = _chain_agrees()
+    assert not ok
+
+
+def test_chain_pin_catches_x_carried_forward(monkeypatch):
+    """Planted mistake: the loop carries the normalised input x to the next
+    layer instead of h_out.  The chain and identity pins both fail."""
+    real = O.moe_layer
+
+    def carries_x(h, W, layer, dims, ftype=np.float64):
+        r = dict(real(h, W, layer, dims, ftype))
+        r["h_out"] = r["x"]
+        return r
+
+    monkeypatch.setattr(O, "moe_layer", carries_x)
+    ok, _ = _chain_agrees()
+    assert not ok
+    dims, W = _stack_weights("f32")
+    W["w_down"][...] = 0
+    W["ws_down"][...] = 0
+    h = synth.make_hidden(dims, 3, seed=12)
+    assert not np.array_equal(O.forward_tokens(h, W, dims, lm_head=False)["h_out"], O.widen(h, "f32"))
+
+
+def test_float32_working_precision_tracks_float64_on_one_layer():
+    """The same algorithm at float32 working precision (the precision of a
+    plain fp32 CPU implementation) stays within fp32 accumulation error of the
+    float64 run: the two differ only in rounding, not in arithmetic."""
+    dims, W = _stack_weights("f32", layers=1)
+    h = O.widen(synth.make_hidden(dims, 16, seed=14), "f32")
+    r64 = O.moe_layer(h, W, 0, dims)
+    r32 = O.moe_layer(h, W, 0, dims, ftype=np.float32)
+    same = np.all(np.sort(r64["ids"], 1) == np.sort(r32["ids"], 1), axis=1)
+    assert same.mean() >= 0.9
+    err = np.abs(r32["y"] - r64["y"]).max(axis=1) / np.abs(r64["y"]).max(axis=1)
+    assert np.all(err[same] < 1e-5), err[same].max()
+
+
+def test_lossless_on_a_three_layer_model():
+    """Losslessness (the accept rule commits exactly the greedy tokens) on a
+    stack of three layers, so the loop over layers is part of both sides."""
+    dims, W = _stack_weights("f32", layers=3, seed=0)
+    emb = synth.make_embedding(dims, seed=0)
+    table = _greedy_table(dims, W, emb)
+    start, n = 29, 120
+    greedy = [start]
+    for _ in range(n):
+        greedy.append(int(table[greedy[-1]]))
+    spec, steps = _spec_decode(dims, W, emb, start, n, K=3, p=0.6, seed=5)
+    assert spec == greedy[1:]
+    assert steps < n
