@@ -36,7 +36,17 @@ def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 @dataclass
 class Tally:
+    """forced=False (a stack run end to end on both sides): a token with a
+    near-tie anywhere is dropped from every later check, since from there
+    the two sides may compute on different inputs.  forced=True (teacher
+    forcing: every layer and the LM head of the oracle are fed the GPU's own
+    input): the inputs agree by construction, so a near-tie drops a token
+    only where the two sides actually decided differently, and only from the
+    checks that difference invalidates: a routing difference skips that
+    layer's row check, an argmax difference the sequence's commit check.  In
+    both modes `excluded` marks the tokens not checked to the end."""
     T: int
+    forced: bool = False
     excluded: np.ndarray = None
     near_ties: int = 0
     tolerated: int = 0
@@ -45,6 +55,11 @@ class Tally:
     def __post_init__(self):
         if self.excluded is None:
             self.excluded = np.zeros(self.T, bool)
+        self._skip_rows = np.zeros(self.T, bool)     # forced: this layer's routing differed
+        self._argmax_off = np.zeros(self.T, bool)    # forced: the argmax differed (near-tie)
+
+    def _live(self):
+        return np.ones(self.T, bool) if self.forced else ~self.excluded
 
     def routing(self, layer, gpu_ids, ref_ids, ref_margin, threshold=MARGIN, ill=None):
         gpu_sets = np.sort(np.asarray(gpu_ids), axis=1)
@@ -53,18 +68,22 @@ class Tally:
         near = np.asarray(ref_margin) < threshold
         if ill is not None:
             near = near | ill
-        live = ~self.excluded
+        live = self._live()
         self.near_ties += int(np.sum(near & live))
         self.tolerated += int(np.sum(differ & near & live))
         bad = np.flatnonzero(differ & ~near & live)
         for t in bad:
             self.failures.append(f"layer {layer} token {t}: gpu {gpu_sets[t]} oracle {ref_sets[t]} "
                                  f"(margin {ref_margin[t]:.3g})")
-        self.excluded |= near | differ
+        if self.forced:
+            self._skip_rows = differ
+            self.excluded |= differ
+        else:
+            self.excluded |= near | differ
 
     def rows(self, what, gpu, ref, tol):
         err = row_rel_err(gpu, ref)
-        live = ~self.excluded
+        live = ~self._skip_rows if self.forced else ~self.excluded
         bad = np.flatnonzero(live & (err > tol))
         for t in bad:
             self.failures.append(f"{what} token {t}: rel err {err[t]:.3g} > {tol}")
@@ -75,17 +94,22 @@ class Tally:
         if ill is not None:
             near = near | ill
         differ = np.asarray(gpu_g) != np.asarray(ref_g)
-        live = ~self.excluded
+        live = self._live()
         self.near_ties += int(np.sum(near & live))
         self.tolerated += int(np.sum(differ & near & live))
         for t in np.flatnonzero(differ & ~near & live):
             self.failures.append(f"argmax token {t}: gpu {gpu_g[t]} oracle {ref_g[t]} "
                                  f"(margin {ref_margin[t]:.3g})")
-        self.excluded |= near | differ
+        if self.forced:
+            self._argmax_off |= differ
+            self.excluded |= differ
+        else:
+            self.excluded |= near | differ
 
     def commits(self, B, K, gpu, ref):
         """gpu/ref: dicts with n_accepted [B], committed [B,K+1], n_committed [B]."""
-        seq_ok = ~self.excluded.reshape(B, K + 1).any(axis=1)
+        off = self._argmax_off if self.forced else self.excluded
+        seq_ok = ~off.reshape(B, K + 1).any(axis=1)
         for key in ("n_accepted", "committed", "n_committed"):
             g = np.asarray(gpu[key]).reshape(B, -1)
             r = np.asarray(ref[key]).reshape(B, -1)
@@ -93,11 +117,23 @@ class Tally:
                 self.failures.append(f"{key} seq {b}: gpu {g[b]} oracle {r[b]}")
         return int(seq_ok.sum())
 
-    def assert_ok(self, label=""):
+    @property
+    def checked(self) -> int:
+        return int(self.T - self.excluded.sum())
+
+    def assert_ok(self, label="", min_checked=None):
+        """No failures, and (so that a comparison cannot pass by excluding
+        everything) at least a fraction min_checked of the tokens checked to
+        the end: by default 3/4 of the tokens (end to end through 12 layers
+        about 15% of tokens meet a near-tie; teacher-forced only the far
+        fewer where the two sides then decide differently are dropped)."""
+        if min_checked is None:
+            min_checked = 0.75
         msg = f"{label}: {len(self.failures)} failures, near-ties {self.near_ties}, " \
-              f"tolerated mismatches {self.tolerated}, excluded tokens {int(self.excluded.sum())}/{self.T}"
+              f"tolerated mismatches {self.tolerated}, checked tokens {self.checked}/{self.T}"
         print(msg)
         assert not self.failures, msg + "\n" + "\n".join(self.failures[:20])
+        assert self.checked >= min_checked * self.T, f"{msg}: fewer than {min_checked:.0%} checked"
 
 
 def stack_conditioning(ref64, ref32):
@@ -114,3 +150,32 @@ def stack_conditioning(ref64, ref32):
         dz = np.abs(ref64["logits"] - ref32["logits"]).max(axis=1)
         final = (np.maximum(MARGIN, 4 * dz), np.asarray(ref64["argmax"]) != np.asarray(ref32["argmax"]))
     return layers, final
+
+
+def forced_stack(bd, torch, dims, W, model, h_dev, rows, label, tally=None, ids_expect=None):
+    """Teacher-forced walk of the layer stack on the device rows h_dev [T, d]:
+    moe_layer_forward layer by layer on the GPU, and at every layer the
+    oracle's layer fed the GPU's own input rows `rows` must route like the GPU
+    (single-layer near-tie rule) and agree on the output rows.  Then the
+    oracle's LM head on the GPU's final rows.  ids_expect [L, T, k]: routing
+    the chain must reproduce bit for bit (a verify step's).  Returns the
+    tally, the GPU's final rows (host) and the oracle's LM-head result."""
+    from oracle import moe_oracle as O
+
+    rows = np.asarray(rows)
+    tally = tally if tally is not None else Tally(len(rows), forced=True)
+    cur = h_dev
+    for layer in range(dims.n_layers):
+        lo = bd.run_layer_forward(model, layer, cur)
+        torch.cuda.synchronize()
+        gid = bd.to_host(lo["topk_ids"])
+        if ids_expect is not None:
+            assert np.array_equal(gid, ids_expect[layer]), f"{label}: layer {layer}: chain and step route differently"
+        ref = O.moe_layer(O.widen(bd.to_host(cur), dims.dtype)[rows], W, layer, dims)
+        tally.routing(layer, gid[rows], ref["ids"], ref["margin"])
+        tally.rows(f"{label} layer {layer} h_out", O.widen(bd.to_host(lo["h_out"]), dims.dtype)[rows],
+                   ref["h_out"], TOL[dims.dtype])
+        cur = lo["h_out"]
+    h_fin = bd.to_host(cur)
+    lm = O.lm_head_argmax(O.widen(h_fin, dims.dtype)[rows], W["final_norm"], W["lm_head"], dims)
+    return tally, h_fin, lm
