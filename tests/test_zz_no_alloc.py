@@ -79,3 +79,39 @@ def test_noalloc_matches_workspace_call_full_width(bd):
         _noalloc(bd, model, bd.to_device(synth.make_hidden(dims, B * (K + 1), seed=7)),
                  bd.to_device(np.zeros((B, K), np.int32)), B, K)
     assert e.value.code == bd.MV_ERR_WORKSPACE
+
+
+def test_noalloc_in_a_graph(bd):
+    """The no-allocation step captured in a HIP graph (the callers it is for):
+    after one eager call on the device, a captured call replays three times,
+    with eager work on the stream between replays, each time equal to the
+    workspace call bit for bit."""
+    import torch
+
+    dims = synth.TINY_F32
+    W = synth.make_weights(dims, seed=0, gamma="uniform")
+    model = bd.DeviceModel(dims, W, max_tokens=64)
+    B, K = 3, 3
+    h = bd.to_device(synth.make_hidden(dims, B * (K + 1), seed=920))
+    drafts = bd.to_device(np.random.default_rng(9).integers(0, dims.vocab, (B, K)).astype(np.int32))
+    ref = bd.run_verify_step(model, h, drafts, B, K, routing=True)
+    torch.cuda.synchronize()
+    ref = {k: bd.to_host(v) for k, v in ref.items() if v is not None}
+    out = _noalloc(bd, model, h, drafts, B, K)      # eager: the device's scratch is looked up here
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        bd.moe_verify_step_noalloc(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
+                                   out["n_accepted"], out["committed"], out["n_committed"], out["topk_ids"],
+                                   torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for v in out.values():
+            v.fill_(-7)                              # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in KEYS:
+            assert np.array_equal(bd.to_host(out[key]), ref[key]), (rep, key)
+        assert _status_noalloc(bd) == 0
