@@ -203,6 +203,28 @@ def _header(args, wl):
             "scaling": "weak", "vs_baseline": None, "dtype": wl.dims.dtype}
 
 
+def copy_ceiling(torch, mib=512, reps=10):
+    """Device-to-device copy rate, GB/s of bytes read plus bytes written: the
+    ceiling a streaming kernel of the same box can be held against (the copy
+    reads and writes equal amounts; the verify step mostly reads)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def bench_verify(args, wl, W, bd, synth, torch):
     dims = wl.dims
     B, K = wl.batch, wl.k_draft
@@ -262,6 +284,8 @@ def bench_verify(args, wl, W, bd, synth, torch):
         "algorithmic_bytes_per_step": int(nbytes),
         "distinct_experts_per_layer": distinct,
     }
+    copy_gbs = copy_ceiling(torch)
+    roofline.update({"copy_gbs": copy_gbs, "frac_of_copy": round(achieved / copy_gbs, 4)})
     status = bd.step_status(model)
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -559,6 +583,7 @@ def bench_draft(args, wl, W, bd, synth, torch):
         cpu = {"value": round(B * K / dt, 3), "unit": "draft tokens/s", "cores": _cores(), "kind": "oracle",
                "sample": f"one mtp_draft call ({B} sequences, K={K}; float64 numpy oracle)",
                "s_per_call": round(dt, 3)}
+    copy_gbs = copy_ceiling(torch)
     line = {"metric": "draft tokens/s (FastMTP draft block) + % of HBM roofline",
             "value": round(B * K / (ms * 1e-3), 1), "unit": "draft tokens/s"}
     line.update(_header(args, wl))
@@ -570,7 +595,8 @@ def bench_draft(args, wl, W, bd, synth, torch):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "whole mtp_draft call (K x [row norms, projection, FFN, LM head])",
-                     "algorithmic_bytes_per_step": int(nbytes)},
+                     "algorithmic_bytes_per_step": int(nbytes), "copy_gbs": copy_gbs,
+                     "frac_of_copy": round(achieved / copy_gbs, 4)},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 4),
     })
