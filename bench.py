@@ -69,6 +69,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-baseline-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="time moe_verify_step_one_launch (batches of up to 8 rows) instead of moe_verify_step")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time graph replays")
     ap.add_argument("--cpu-baseline-rows", type=int, default=8,
@@ -244,12 +246,16 @@ def bench_verify(args, wl, W, bd, synth, torch):
 
     out = bd.run_verify_step(model, h, drafts, B, K)
 
+    entry = bd.moe_verify_step_one_launch if args.one_launch else bd.moe_verify_step
+
     def step(stream):
-        bd.moe_verify_step(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
-                           out["n_accepted"], out["committed"], out["n_committed"], None,
-                           model.ws, model.ws_bytes, stream)
+        entry(model.cfg, model.weights, B, K, h, drafts, out["h_out"], out["argmax"],
+              out["n_accepted"], out["committed"], out["n_committed"], None,
+              model.ws, model.ws_bytes, stream)
 
     run = step
+    if args.graph and args.one_launch:
+        raise SystemExit("--graph and --one-launch are separate measurements")
     if args.graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -311,6 +317,7 @@ def bench_verify(args, wl, W, bd, synth, torch):
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_ms_per_step": round(t_enq / args.steps * 1e3, 4),
         "graph": bool(args.graph),
+        "entry_point": "moe_verify_step_one_launch" if args.one_launch else "moe_verify_step",
         "timing": _timing(args),
     })
     return line

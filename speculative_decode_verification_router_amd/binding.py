@@ -20,7 +20,7 @@ MV_F32, MV_BF16 = 0, 1
 MV_OK, MV_ERR_NULL, MV_ERR_SHAPE, MV_ERR_UNSUPPORTED, MV_ERR_WORKSPACE, MV_ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTED = ("mv_workspace_bytes", "moe_layer_forward", "moe_verify_step", "moe_verify_step_noalloc",
-            "spec_accept",
+            "moe_verify_step_one_launch", "spec_accept",
             "mtp_workspace_bytes", "mtp_draft", "mv_choose_k", "mv_step_bytes", "mv_step_status",
             "mv_set_spin_limit", "mv_last_error")
 
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_step.restype = ctypes.c_int
     lib.moe_verify_step_noalloc.argtypes = [cfgp, wp, I, I, P, P, P, P, P, P, P, P, P]
     lib.moe_verify_step_noalloc.restype = ctypes.c_int
+    lib.moe_verify_step_one_launch.argtypes = [cfgp, wp, I, I, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_verify_step_one_launch.restype = ctypes.c_int
     lib.spec_accept.argtypes = [I, I, P, P, P, P, P, P]
     lib.spec_accept.restype = ctypes.c_int
     mwp = ctypes.POINTER(MtpWeights)
@@ -151,6 +153,15 @@ def moe_verify_step(cfg: MvConfig, weights: MvWeights, B: int, K: int, h_in, dra
                                   _ptr(drafts), _ptr(h_out), _ptr(argmax), _ptr(n_accepted),
                                   _ptr(committed), _ptr(n_committed), _ptr(dbg_topk_ids),
                                   _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_verify_step_one_launch(cfg: MvConfig, weights: MvWeights, B: int, K: int, h_in, drafts, h_out,
+                               argmax, n_accepted, committed, n_committed, dbg_topk_ids=None, ws=None,
+                               ws_bytes: int = 0, stream=None) -> None:
+    _check(load().moe_verify_step_one_launch(ctypes.byref(cfg), ctypes.byref(weights), B, K, _ptr(h_in),
+                                             _ptr(drafts), _ptr(h_out), _ptr(argmax), _ptr(n_accepted),
+                                             _ptr(committed), _ptr(n_committed), _ptr(dbg_topk_ids),
+                                             _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_verify_step_noalloc(cfg: MvConfig, weights: MvWeights, B: int, K: int, h_in, drafts, h_out,
@@ -306,8 +317,9 @@ def to_host(t) -> np.ndarray:
 
 
 def run_verify_step(model: DeviceModel, h_in, drafts, B: int, K: int, h_out: bool = True,
-                    routing: bool = False, stream=None) -> Dict[str, object]:
-    """Allocate the outputs and enqueue one moe_verify_step (no sync)."""
+                    routing: bool = False, stream=None, one_launch: bool = False) -> Dict[str, object]:
+    """Allocate the outputs and enqueue one moe_verify_step, or with
+    one_launch moe_verify_step_one_launch (no sync)."""
     import torch
 
     dev = h_in.device
@@ -321,9 +333,10 @@ def run_verify_step(model: DeviceModel, h_in, drafts, B: int, K: int, h_out: boo
         topk_ids=(torch.empty((model.dims.n_layers, T, model.dims.top_k), dtype=torch.int32,
                               device=dev) if routing else None),
     )
-    moe_verify_step(model.cfg, model.weights, B, K, h_in, drafts, out["h_out"], out["argmax"],
-                    out["n_accepted"], out["committed"], out["n_committed"], out["topk_ids"],
-                    model.ws, model.ws_bytes, stream)
+    step = moe_verify_step_one_launch if one_launch else moe_verify_step
+    step(model.cfg, model.weights, B, K, h_in, drafts, out["h_out"], out["argmax"],
+         out["n_accepted"], out["committed"], out["n_committed"], out["topk_ids"],
+         model.ws, model.ws_bytes, stream)
     return out
 
 

@@ -11,6 +11,7 @@
 
 #include "moe_verify.h"
 #include "mv_internal.h"
+#include "lm_core.h"
 
 #define MV_API extern "C" __attribute__((visibility("default")))
 
@@ -68,7 +69,7 @@ int max_tiles(const mv_config &c, int T) { return max_tiles(c, T, tile_rows(c, T
 
 struct Layout {
   size_t status, hbuf, hbuf2, hbuf3, x, ids, gates, seg, tiles, tinfo, rows, a, slots, argkey, done, bcnt, logits, tdone,
-      total;
+      ol_ctr, ol_args, total;
 };
 
 // Words of one set of fused-launch counters: one per tile and one per copy of
@@ -110,6 +111,10 @@ Layout layout(const mv_config &c, int T) {
   L.logits = take(static_cast<size_t>(T) * 64 * 4);
   // two sets of fused-launch counters (tiles, then the routing copies)
   L.tdone = take(2 * done_set_words(c, T) * 4);
+  // the one-launch step (batches routed to logits): its counters and arguments
+  const bool one = T <= mv::kLogitsMaxT && c.n_layers <= mv::kOneLaunchMaxLayers;
+  L.ol_ctr = take(one ? mv::one_launch_counter_words(c.n_layers, max_tiles(c, T, mv::kTileM)) * 4 : 0);
+  L.ol_args = take(one ? sizeof(mv::OneLaunchDev) : 0);
   L.total = off;
   return L;
 }
@@ -275,6 +280,29 @@ struct Step {
           float *y_moe = nullptr, bool logits = false, const mv::RouteArgs *ra = nullptr,
           const mv::CombineArgs *ca = nullptr) const {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
+    mv::ExpertArgs e = expert_args(layer, ids, gates, logits);
+    const int mt = max_tiles(c, T);
+    if (logits) return hip_status(mv::launch_ffn_small(c.dtype, e, ra, ca, mt, s));
+    const Path path = path_for(c, T);
+    int rc = hip_status(path == kGemmTiles  ? mv::launch_gemm_gate_up(e, mt, s)
+                        : path == kMidTiles ? mv::launch_gate_up_mid(c.dtype, e, mt, s)
+                                            : mv::launch_gate_up(c.dtype, e, mt, s));
+    if (rc) return rc;
+    e.w_routed = lp.down;
+    e.w_shared = lp.sdown;
+    if (path == kGemmTiles) {
+      if ((rc = hip_status(mv::launch_gemm_down(e, mt, s)))) return rc;
+      mv::CombineArgs cb{h_src, h_dst, slots(), y_moe};
+      return hip_status(mv::launch_gemm_down_shared(e, cb, s));
+    }
+    return hip_status(path == kMidTiles ? mv::launch_down_mid(c.dtype, e, mt, s)
+                                        : mv::launch_down(c.dtype, e, mt, s));
+  }
+
+  // Expert-launch arguments of `layer` (gate/up weights; with `logits`, the
+  // fused launch's: down weights, top-k outputs, counter set layer % 2).
+  mv::ExpertArgs expert_args(int layer, int *ids, float *gates, bool logits) const {
+    const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e{};
     e.T = T;
     e.d = c.d_model;
@@ -294,7 +322,6 @@ struct Step {
     e.group_in_block = small() ? 1 : 0;
     e.gates = gates;
     e.slots = slots();
-    const int mt = max_tiles(c, T);
     e.w_routed = lp.gu;
     e.w_shared = lp.sgu;
     if (logits) {  // gate/up and down in one launch
@@ -310,22 +337,8 @@ struct Step {
       e.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
       e.w_routed_down = lp.down;
       e.w_shared_down = lp.sdown;
-      return hip_status(mv::launch_ffn_small(c.dtype, e, ra, ca, mt, s));
     }
-    const Path path = path_for(c, T);
-    int rc = hip_status(path == kGemmTiles  ? mv::launch_gemm_gate_up(e, mt, s)
-                        : path == kMidTiles ? mv::launch_gate_up_mid(c.dtype, e, mt, s)
-                                            : mv::launch_gate_up(c.dtype, e, mt, s));
-    if (rc) return rc;
-    e.w_routed = lp.down;
-    e.w_shared = lp.sdown;
-    if (path == kGemmTiles) {
-      if ((rc = hip_status(mv::launch_gemm_down(e, mt, s)))) return rc;
-      mv::CombineArgs cb{h_src, h_dst, slots(), y_moe};
-      return hip_status(mv::launch_gemm_down_shared(e, cb, s));
-    }
-    return hip_status(path == kMidTiles ? mv::launch_down_mid(c.dtype, e, mt, s)
-                                        : mv::launch_down(c.dtype, e, mt, s));
+    return e;
   }
 };
 
@@ -471,6 +484,64 @@ int scratch_on_device(void **out) {
 
 }  // namespace
 
+// The verify step of a batch routed to logits as one launch: the setup kernel
+// writes every virtual block's arguments and clears the counters, then
+// k_one_launch runs the layers' fused launches, the final norm and the LM
+// head with the accept rule as virtual blocks of resident blocks.  Buffers
+// and arithmetic are those of verify_launches, so the results are
+// bit-identical to moe_verify_step's.
+int one_launch_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K, const void *h_in,
+                    const int32_t *drafts, void *h_out, int32_t *argmax, int32_t *n_accepted, int32_t *committed,
+                    int32_t *n_committed, int32_t *dbg_topk_ids, void *ws, void *stream) {
+  const int T = B * (K + 1), L = cfg->n_layers, k = cfg->top_k;
+  if (T > mv::kLogitsMaxT || L > mv::kOneLaunchMaxLayers)
+    return fail(MV_ERR_UNSUPPORTED, "the one-launch verify step takes at most 8 rows (B*(K+1)) and 16 layers");
+  Step st{*cfg, *w, T, static_cast<char *>(ws), layout(*cfg, T), static_cast<hipStream_t>(stream)};
+  void *hbuf = h_out ? h_out : static_cast<void *>(st.ws + st.L.hbuf);
+  float *gates = st.gates();
+  const int mt = max_tiles(*cfg, T);
+  mv::OneLaunchArgs a{};
+  a.e = st.expert_args(0, nullptr, gates, true);
+  a.e.n_done = 0;  // the setup kernel clears every counter
+  a.e.done_next = nullptr;
+  a.r = st.route_args(0, mv::kRoute, nullptr, gates);
+  a.r.mode = mv::kLogits;
+  a.r.logits = st.logits();
+  a.f = st.route_args(L - 1, mv::kFinal, nullptr, nullptr);
+  a.slots = st.slots();
+  a.ctr = reinterpret_cast<unsigned *>(st.ws + st.L.ol_ctr);
+  a.L = L;
+  a.max_tiles = mt;
+  a.n_route = T * ((cfg->n_routed + mv::kRouteGroup - 1) / mv::kRouteGroup);
+  a.n_lm = (cfg->vocab + mv::kLmRowsPerBlock - 1) / mv::kLmRowsPerBlock;
+  a.set_lines = mt + mv::kRouteCopies + 1;
+  unsigned *lm_done = a.ctr + (static_cast<size_t>(L) * a.set_lines + 1) * mv::kDoneStride;
+  const mv::AcceptArgs aa{B, K, st.argkey(), nullptr, argmax, drafts, n_accepted, committed, n_committed};
+  a.lm = mv::LmArgs{T, cfg->d_model, cfg->vocab, st.ws + st.L.x, w->lm_head, st.argkey(), lm_done, aa};
+  const void *cur = h_in;  // the same hidden-state buffers as verify_launches
+  for (int layer = 0; layer < L; ++layer) {
+    const LayerPtrs lp = layer_ptrs(*cfg, *w, layer);
+    mv::StepLayer &sl = a.layer[layer];
+    sl = mv::StepLayer{lp.gu, lp.down, lp.sgu, lp.sdown, lp.norm, lp.router, lp.bias,
+                       dbg_topk_ids ? dbg_topk_ids + static_cast<size_t>(layer) * T * k
+                                    : reinterpret_cast<int *>(st.ws + st.L.ids),
+                       h_in, nullptr};
+    if (layer == 0) continue;
+    void *dst = (L - layer) % 2 == 0 ? hbuf : static_cast<void *>(st.ws + st.L.hbuf2);
+    if (dst == cur) dst = st.ws + st.L.hbuf3;
+    sl.h_src = cur;
+    sl.h_dst = dst;
+    cur = dst;
+  }
+  a.h_last = cur;
+  a.h_final = hbuf;
+  const size_t smem = mv::one_launch_smem(cfg->dtype, T, cfg->d_model, cfg->d_ff);
+  const int blocks = mv::one_launch_blocks(cfg->dtype, smem);
+  if (blocks <= 0) return fail(MV_ERR_HIP, "the one-launch verify step cannot be made resident on this device");
+  return hip_status(mv::launch_one_launch(cfg->dtype, a, reinterpret_cast<mv::OneLaunchDev *>(st.ws + st.L.ol_args),
+                                          st.status(), blocks, smem, st.s));
+}
+
 MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
                            const void *h_in, const int32_t *drafts, void *h_out, int32_t *argmax,
                            int32_t *n_accepted, int32_t *committed, int32_t *n_committed,
@@ -481,6 +552,18 @@ MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
   if ((rc = check_ws(cfg, B * (K + 1), ws, ws_bytes))) return rc;
   return verify_launches(cfg, w, B, K, h_in, drafts, h_out, argmax, n_accepted, committed, n_committed,
                          dbg_topk_ids, ws, stream);
+}
+
+MV_API int moe_verify_step_one_launch(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,
+                                      const void *h_in, const int32_t *drafts, void *h_out, int32_t *argmax,
+                                      int32_t *n_accepted, int32_t *committed, int32_t *n_committed,
+                                      int32_t *dbg_topk_ids, void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  int rc = check_verify(cfg, w, B, K, h_in, drafts, argmax, n_accepted, committed, n_committed);
+  if (rc || B == 0) return rc;
+  if ((rc = check_ws(cfg, B * (K + 1), ws, ws_bytes))) return rc;
+  return one_launch_step(cfg, w, B, K, h_in, drafts, h_out, argmax, n_accepted, committed, n_committed, dbg_topk_ids,
+                         ws, stream);
 }
 
 MV_API int moe_verify_step_noalloc(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,

@@ -201,7 +201,9 @@ struct DownPart {
     load_batch<T, U>(q, b, w_lo, w_hi);
   }
   // tile_rows[row]: the pair id (t*nslot + slot) of tile row `row`; gates:
-  // [T, k] softmax gates of the routed pairs.
+  // [T, k] softmax gates of the routed pairs.  kThrough: the slots are
+  // written through (read by later blocks of the same launch).
+  template <bool kThrough = false>
   __device__ __forceinline__ void finish(const ExpertArgs &p, const TileInfo &ti, const T *arow,
                                          float (*half_acc)[64][4], int tid, const int *tile_rows,
                                          const float *gates) {
@@ -221,7 +223,10 @@ struct DownPart {
         const int pair = tile_rows[row];
         const int tok = pair / p.nslot, s = pair - tok * p.nslot;
         const float w = s < p.k ? gates[tok * p.k + s] : 1.0f;
-        p.slots[static_cast<size_t>(pair) * d + n0 + (lane & 15)] = w * (acc[i] + half_acc[slice][lane][i]);
+        float *dst = p.slots + static_cast<size_t>(pair) * d + n0 + (lane & 15);
+        const float v = w * (acc[i] + half_acc[slice][lane][i]);
+        if constexpr (kThrough) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = v;
       }
     }
   }

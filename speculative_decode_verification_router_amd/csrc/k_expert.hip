@@ -9,6 +9,7 @@
 // logits run gate/up and down in one launch (k_ffn_small), taking the top-k
 // in every block.
 #include "expert_core.h"
+#include "lm_core.h"
 
 namespace mv {
 
@@ -221,24 +222,25 @@ __device__ __forceinline__ void wait_count(const unsigned *ctr, unsigned target,
 // n_route > 0: the launch also routes this layer (ra, ca): its first n_route
 // blocks (token, expert group) run route_fused, and the other blocks wait
 // for them (shared gate/up blocks after requesting their first weights).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs ra, CombineArgs ca, int max_tiles,
-                                                        int n_route) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ SmallTiles st;
-  __shared__ float xacc[2][64][4];
+// Block `vb` of the launch (blockIdx.x of k_ffn_small, or a virtual block of
+// the one-launch step); kInLaunch: the one-launch step, where the routing's
+// sources were written by blocks of the same launch and the slots are read by
+// later blocks of it.
+template <typename T, bool kInLaunch>
+__device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const CombineArgs &ca, int max_tiles,
+                                int n_route, int vb, unsigned char *smem, SmallTiles &st, float (*xacc)[64][4]) {
   constexpr int VN = Vec<T>::N;
   const int d = p.d, F = p.F, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (blockIdx.x == 0)  // the next launch's counters (this launch's were cleared before it started)
+  if (vb == 0)  // the next launch's counters (this launch's were cleared before it started)
     for (int i = tid; i < p.n_done; i += blockDim.x) p.done_next[static_cast<size_t>(i) * kDoneStride] = 0u;
-  if (static_cast<int>(blockIdx.x) < n_route) {
+  if (vb < n_route) {
     const int G = (p.E + kRouteGroup - 1) / kRouteGroup;
-    route_fused<T>(ra, ca, blockIdx.x / G, blockIdx.x % G, smem, p.route_done, kRouteCopies, kDoneStride);
+    route_fused<T, kInLaunch>(ra, ca, vb / G, vb % G, smem, p.route_done, kRouteCopies, kDoneStride);
     return;
   }
-  const unsigned *route_ctr = p.route_done + static_cast<size_t>(blockIdx.x % kRouteCopies) * kDoneStride;
+  const unsigned *route_ctr = p.route_done + static_cast<size_t>(vb % kRouteCopies) * kDoneStride;
   const int sp_gu = (F + 31) / 32, sp_dn = (d + 31) / 32;
-  const int b0 = blockIdx.x - n_route;
+  const int b0 = vb - n_route;
   const bool gu = b0 < sp_gu * max_tiles;
   const int b = gu ? b0 : b0 - sp_gu * max_tiles;
   const int sp = gu ? sp_gu : sp_dn, y = b / sp, pair = b - y * sp;
@@ -328,7 +330,162 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs 
     }
   }
   __syncthreads();
-  part.finish(p, ti, A + arow * (F + VN) + (lane >> 4) * VN, xacc, tid, st.rows[w], st.gates);
+  part.template finish<kInLaunch>(p, ti, A + arow * (F + VN) + (lane >> 4) * VN, xacc, tid, st.rows[w], st.gates);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs ra, CombineArgs ca, int max_tiles,
+                                                        int n_route) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ SmallTiles st;
+  __shared__ float xacc[2][64][4];
+  ffn_small_block<T, false>(p, ra, ca, max_tiles, n_route, static_cast<int>(blockIdx.x), smem, st, xacc);
+}
+
+// ------------------------------------------------- one-launch verify step
+//
+// The verify step of a batch routed to logits as one launch of resident
+// blocks.  Its launches become virtual blocks, numbered in launch order: per
+// layer the fused launch's blocks (routing, gate/up, down; layer 0 routes
+// inside it too), then one final-norm block per token, then the LM head's
+// blocks, whose last one applies the accept rule.  A resident block that is
+// free takes the next virtual block number from a counter, so the numbers
+// are handed out in increasing order, and runs it with the code of the
+// launch it stands for.  Every wait is for virtual blocks of lower number: a
+// layer's routing for every expert block of the previous layer (which also
+// keeps each buffer the layers share from being overwritten while it is
+// read), its expert blocks as in the fused launch, the final norm for the
+// last layer, the LM head for the final norm.  So the lowest unfinished
+// virtual block that has been taken has all its inputs, and its block is
+// running it (every block runs its virtual blocks in increasing order, and
+// one that is free takes a new one): with all
+// blocks resident (a cooperative launch) the launch cannot deadlock, and the
+// waits are bounded as in the fused launch.  Data another block of the launch
+// reads is written through and read with agent-scope loads.  Per virtual
+// block the arithmetic is that of the block it stands for (route_fused is
+// route_block's in both modes), so results are bit-identical to the launches.
+// One block: every layer's arguments from the shared ones and the layer's
+// pointers; all blocks: the counters and the status word cleared.
+__global__ __launch_bounds__(256) void k_one_launch_setup(OneLaunchArgs a, OneLaunchDev *dev, unsigned *status) {
+  const size_t n = one_launch_counter_words(a.L, a.max_tiles);
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    a.ctr[i] = 0u;
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0) *status = 0u;
+  const int l = threadIdx.x;
+  if (l < a.L) {
+    const StepLayer &sl = a.layer[l];
+    unsigned *set = a.ctr + static_cast<size_t>(l) * a.set_lines * kDoneStride;
+    OneLaunchLayer ly;
+    ly.e = a.e;
+    ly.e.w_routed = sl.gu;
+    ly.e.w_shared = sl.sgu;
+    ly.e.w_routed_down = sl.down;
+    ly.e.w_shared_down = sl.sdown;
+    ly.e.ids_out = sl.ids;
+    ly.e.tile_done = set;
+    ly.e.route_done = set + static_cast<size_t>(a.max_tiles) * kDoneStride;
+    ly.r = a.r;
+    ly.r.gamma = sl.norm;
+    ly.r.router_w = sl.router;
+    ly.r.router_b = sl.bias;
+    ly.c = CombineArgs{sl.h_src, sl.h_dst, l ? a.slots : nullptr, nullptr};
+    dev->layer[l] = ly;
+  }
+  if (threadIdx.x == 0) {
+    dev->f = a.f;
+    dev->fc = CombineArgs{a.h_last, a.h_final, a.slots, nullptr};
+    dev->lm = a.lm;
+  }
+}
+
+// Virtual blocks of the one-launch step.
+template <typename T>
+__device__ __forceinline__ void one_launch_layer_block(const OneLaunchLayer &ly, int max_tiles, int n_route,
+                                                                int local, unsigned char *smem, SmallTiles &st,
+                                                                float (*xacc)[64][4]) {
+  ffn_small_block<T, true>(ly.e, ly.r, ly.c, max_tiles, n_route, local, smem, st, xacc);
+}
+template <typename T>
+__device__ __forceinline__ void one_launch_final_block(const OneLaunchDev *dev, int t, unsigned char *smem,
+                                                                unsigned *final_ctr) {
+  route_fused<T, true, true>(dev->f, dev->fc, t, 0, smem, final_ctr, 1, kDoneStride);
+}
+template <typename T>
+__device__ __forceinline__ void one_launch_lm_block(const LmArgs &p, int vblk, int n_lm, const unsigned *ready,
+                                                             unsigned *err, int spin_limit, unsigned char *smem,
+                                                             unsigned long long (*red)[kTileM]) {
+  constexpr int VN = Vec<T>::N;
+  const int tid = threadIdx.x, T_ = p.T, d = p.d;
+  LmStream<T> ls;
+  ls.begin(p, vblk, tid);  // weights requested before x_f is ready
+  wait_count(ready, static_cast<unsigned>(T_), err, spin_limit);
+  __syncthreads();
+  const int nvec = d / VN, lda = d + VN;
+  T *A = reinterpret_cast<T *>(smem);  // rows [0, T) of x_f, then a zero row
+  const T *xf = static_cast<const T *>(p.xf);
+  for (int i = tid; i < (T_ + 1) * nvec; i += blockDim.x) {
+    const int rr = i / nvec, cc = i - rr * nvec;
+    st16(A + rr * lda + cc * VN,
+         rr < T_ ? ld16_agent(xf + static_cast<size_t>(rr) * d + cc * VN) : make_uint4(0, 0, 0, 0));
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  const int arow = (lane & 15) < T_ ? (lane & 15) : T_;
+  ls.finish(p, 0, T_, A + arow * lda + (lane >> 4) * VN, red, tid);
+  lm_block_done(p, static_cast<unsigned>(n_lm));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void k_one_launch(const OneLaunchDev *__restrict__ dev, int L, int T_,
+                                                            int n_route, int n_expert, int max_tiles, int n_lm,
+                                                            int set_lines, unsigned *ctr, unsigned *err,
+                                                            int spin_limit) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ SmallTiles st;
+  __shared__ float xacc[2][64][4];
+  __shared__ unsigned long long red[kLmWaves][kTileM];
+  const int per_layer = n_route + n_expert;
+  const int n_layers_vb = L * per_layer, total = n_layers_vb + T_ + n_lm;
+  unsigned *final_ctr = ctr + static_cast<size_t>(L) * set_lines * kDoneStride;
+  // Each block takes the next virtual block number from a counter when it is
+  // free (in increasing order, as the hardware hands out a launch's blocks);
+  // one loop per kind, in order (each loop's registers are its own): the
+  // layers', the final norms', the LM head's.
+  __shared__ int vb_s;
+  unsigned *vb_ctr = final_ctr + 2 * kDoneStride;
+  auto take = [&]() {
+    __syncthreads();  // the previous virtual block's LDS and vb_s
+    if (threadIdx.x == 0)
+      vb_s = static_cast<int>(__hip_atomic_fetch_add(vb_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    return vb_s;
+  };
+  int vb = take();
+  for (; vb < n_layers_vb; vb = take()) {
+    const int l = vb / per_layer, local = vb - l * per_layer;
+    unsigned *done_l = ctr + (static_cast<size_t>(l) * set_lines + max_tiles + kRouteCopies) * kDoneStride;
+    if (local < n_route && l > 0) {  // the previous layer's expert blocks have finished
+      wait_count(done_l - static_cast<size_t>(set_lines) * kDoneStride, static_cast<unsigned>(n_expert), err,
+                 spin_limit);
+      __syncthreads();
+    }
+    one_launch_layer_block<T>(dev->layer[l], max_tiles, n_route, local, smem, st, xacc);
+    if (local >= n_route) {  // count this expert block of layer l
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // its slots have completed
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(done_l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  for (; vb < n_layers_vb + T_; vb = take()) {  // final combine and norm of one token
+    wait_count(final_ctr - static_cast<size_t>(set_lines - max_tiles - kRouteCopies) * kDoneStride,
+               static_cast<unsigned>(n_expert), err, spin_limit);
+    __syncthreads();
+    one_launch_final_block<T>(dev, vb - n_layers_vb, smem, final_ctr);
+  }
+  for (; vb < total; vb = take())  // LM-head blocks over all T rows (T <= 16)
+    one_launch_lm_block<T>(dev->lm, vb - n_layers_vb - T_, n_lm, final_ctr, err, spin_limit, smem, red);
 }
 
 // ------------------------------------------------------------ medium batches
@@ -531,6 +688,41 @@ hipError_t launch_ffn_small(int dtype, const ExpertArgs &a, const RouteArgs *ra,
     hipLaunchKernelGGL(k_ffn_small<float>, grid, dim3(kThreads), smem, s, a, r0, c0, max_tiles, n_route);
   }
   return hipGetLastError();
+}
+
+size_t one_launch_smem(int dtype, int T, int d, int F) {
+  const size_t es = dtype == 1 ? 2 : 4;
+  const size_t rows = (T < kTileM ? T : kTileM) + 1;
+  size_t smem = rows * ((d > F ? d : F) + 16 / es) * es;  // fused expert blocks and the LM head's x_f rows
+  const size_t route = route_smem(1, d, static_cast<int>(es)).total;
+  return smem > route ? smem : route;
+}
+
+int one_launch_blocks(int dtype, size_t smem) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))
+    return 0;
+  const void *f = dtype == 1 ? reinterpret_cast<const void *>(k_one_launch<bf16_t>)
+                             : reinterpret_cast<const void *>(k_one_launch<float>);
+  if (smem > 48 * 1024) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kThreads, smem) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
+hipError_t launch_one_launch(int dtype, const OneLaunchArgs &a, OneLaunchDev *dev, unsigned *status, int blocks,
+                             size_t smem, hipStream_t s) {
+  hipLaunchKernelGGL(k_one_launch_setup, dim3(16), dim3(256), 0, s, a, dev, status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const OneLaunchDev *cdev = dev;
+  int L = a.L, T = a.e.T, n_route = a.n_route, mt = a.max_tiles, n_lm = a.n_lm, sl = a.set_lines;
+  int n_expert = ((a.e.F + 31) / 32 + (a.e.d + 31) / 32) * mt;
+  unsigned *ctr = a.ctr, *err = a.e.err;
+  int spin = a.e.spin_limit;
+  void *args[] = {&cdev, &L, &T, &n_route, &n_expert, &mt, &n_lm, &sl, &ctr, &err, &spin};
+  const void *f = dtype == 1 ? reinterpret_cast<const void *>(k_one_launch<bf16_t>)
+                             : reinterpret_cast<const void *>(k_one_launch<float>);
+  return hipLaunchCooperativeKernel(f, dim3(blocks), dim3(kThreads), args, static_cast<unsigned>(smem), s);
 }
 
 }  // namespace mv

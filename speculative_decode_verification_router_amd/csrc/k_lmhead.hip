@@ -14,49 +14,6 @@ namespace mv {
 
 namespace {
 
-// Accept rule for sequence b: n = first j < K with drafts[j] != argmax[j]
-// (else K); committed = argmax[0..n], -1 after; n_committed = n + 1.  With
-// `coherent` the keys are read with agent-scope loads (keys folded by other
-// blocks of the same launch).
-__device__ void accept_sequence(const AcceptArgs &p, int b, bool coherent) {
-  const int K = p.K, base = b * (K + 1);
-  for (int j = 0; j <= K; ++j) {
-    int g;
-    if (p.argkey) {
-      const unsigned long long key =
-          coherent ? __hip_atomic_load(p.argkey + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : p.argkey[base + j];
-      g = static_cast<int>(key_index(key));
-    } else {
-      g = p.argmax_in[base + j];
-    }
-    if (p.argmax_out) p.argmax_out[base + j] = g;
-  }
-  const int *g = p.argkey ? p.argmax_out : p.argmax_in;
-  int n = 0;
-  while (n < K && p.drafts[b * K + n] == g[base + n]) ++n;
-  for (int j = 0; j <= K; ++j) p.committed[base + j] = j <= n ? g[base + j] : -1;
-  p.n_acc[b] = n;
-  p.n_com[b] = n + 1;
-}
-
-// After a block's atomicMax: wait for it to complete, count the block, and
-// in the last block to finish run the accept rule over every sequence.
-// The key updates are device-scope atomics and the last block reads the
-// keys with agent-scope loads, so no cache write-back is needed.
-__device__ void lm_block_done(const LmArgs &p) {
-  if (!p.done) return;
-  __shared__ int last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           gridDim.x * gridDim.y - 1;
-  __syncthreads();
-  if (!last) return;
-  for (int b = threadIdx.x; b < p.accept.B; b += blockDim.x) accept_sequence(p.accept, b, true);
-}
-
 }  // namespace
 
 namespace {
@@ -84,7 +41,7 @@ __global__ __launch_bounds__(256) void k_lm_argmax(LmArgs p) {
   const int lane = threadIdx.x & 63;
   const int arow = (lane & 15) < m ? (lane & 15) : m;
   ls.finish(p, r0, m, A + arow * lda + (lane >> 4) * VN, red, threadIdx.x);
-  lm_block_done(p);
+  lm_block_done(p, gridDim.x * gridDim.y);
 }
 
 // Up to 128 rows: every block takes all rows of its 16*MT-row group, so the
@@ -208,7 +165,7 @@ __global__ __launch_bounds__(64 * kLmMidWaves) void k_lm_argmax_mid(LmArgs p) {
     for (int w = 0; w < kLmMidWaves; ++w) k = red[w][row] > k ? red[w][row] : k;
     if (k != 0ull) atomicMax(p.argkey + rbase + row, static_cast<unsigned long long>(k));
   }
-  lm_block_done(p);
+  lm_block_done(p, gridDim.x * gridDim.y);
 }
 
 // One thread per sequence.

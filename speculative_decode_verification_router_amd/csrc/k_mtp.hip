@@ -52,9 +52,9 @@ __device__ __forceinline__ void tile_inv_rms(int m, int d, float eps, float *par
 #pragma unroll
     for (int u = 0; u < kChunksInFlight; ++u) {
       const int it = it0 + u * static_cast<int>(blockDim.x);
-      float s = 0.f;
+      float s = v[u][0] * v[u][0];
 #pragma unroll
-      for (int i = 0; i < VN; ++i) s += v[u][i] * v[u][i];
+      for (int i = 1; i < VN; ++i) s = __builtin_fmaf(v[u][i], v[u][i], s);
       if (it < m * nvec) part[it] = s;
     }
   }

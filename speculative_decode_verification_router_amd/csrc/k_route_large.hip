@@ -99,9 +99,9 @@ __global__ __launch_bounds__(kRLThreads) void k_route_large(RouteArgs a, const b
       if (r < nt) {
         float f[8];
         unpack(v[u], f, bf16_t());
-        float s = 0.f;
+        float s = f[0] * f[0];  // route_block's order: first square, then fused multiply-adds
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s += f[i] * f[i];
+        for (int i = 1; i < 8; ++i) s = __builtin_fmaf(f[i], f[i], s);
         pl[r * nvec + ch] = s;
       }
       st16(xl + r * ld + ch * 8, v[u]);

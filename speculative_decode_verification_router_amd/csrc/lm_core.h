@@ -101,4 +101,46 @@ struct LmStream {
   }
 };
 
+// Accept rule for sequence b: n = first j < K with drafts[j] != argmax[j]
+// (else K); committed = argmax[0..n], -1 after; n_committed = n + 1.  With
+// `coherent` the keys are read with agent-scope loads (keys folded by other
+// blocks of the same launch).
+__device__ inline void accept_sequence(const AcceptArgs &p, int b, bool coherent) {
+  const int K = p.K, base = b * (K + 1);
+  for (int j = 0; j <= K; ++j) {
+    int g;
+    if (p.argkey) {
+      const unsigned long long key =
+          coherent ? __hip_atomic_load(p.argkey + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : p.argkey[base + j];
+      g = static_cast<int>(key_index(key));
+    } else {
+      g = p.argmax_in[base + j];
+    }
+    if (p.argmax_out) p.argmax_out[base + j] = g;
+  }
+  const int *g = p.argkey ? p.argmax_out : p.argmax_in;
+  int n = 0;
+  while (n < K && p.drafts[b * K + n] == g[base + n]) ++n;
+  for (int j = 0; j <= K; ++j) p.committed[base + j] = j <= n ? g[base + j] : -1;
+  p.n_acc[b] = n;
+  p.n_com[b] = n + 1;
+}
+
+// After a block's atomicMax: wait for it to complete, count the block, and
+// in the last of n_blocks blocks to finish run the accept rule over every
+// sequence.  The key updates are device-scope atomics and the last block
+// reads the keys with agent-scope loads, so no cache write-back is needed.
+__device__ inline void lm_block_done(const LmArgs &p, unsigned n_blocks) {
+  if (!p.done) return;
+  __shared__ int last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_blocks - 1;
+  __syncthreads();
+  if (!last) return;
+  for (int b = threadIdx.x; b < p.accept.B; b += blockDim.x) accept_sequence(p.accept, b, true);
+}
+
 }  // namespace mv

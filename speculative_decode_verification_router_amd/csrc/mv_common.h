@@ -107,6 +107,24 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
 }
 __device__ __forceinline__ void st16(void *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
 
+// 16 bytes written earlier in the same launch by another block: four
+// agent-scope loads, which no stale cache line can answer.
+__device__ __forceinline__ uint4 ld16_agent(const void *p) {
+  const uint32_t *q = static_cast<const uint32_t *>(p);
+  return make_uint4(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                    __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                    __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                    __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// 16 bytes that other blocks of the same launch read: write-through stores.
+__device__ __forceinline__ void st16_through(void *p, const uint4 &v) {
+  uint32_t *q = static_cast<uint32_t *>(p);
+  __hip_atomic_store(q, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One 16x16 MFMA accumulation over the K-window that one 16-byte vector per
 // lane covers: 32 bf16 (one v_mfma_f32_16x16x32_bf16) or 16 fp32 (four
 // v_mfma_f32_16x16x4_f32).  Lane l supplies row (l % 16) of A and column

@@ -4,7 +4,8 @@
 // fp32 elements of a row):
 //   combine   h' = round(h + y),  y = sum of the token's slots in slot order
 //             (routed slots in selection order, then the shared ones)
-//   sumsq     chunk partial p_c = sequential sum of h'^2 over chunk c; lane l
+//   sumsq     chunk partial p_c = sequential sum of h'^2 over chunk c (the
+//             first square, then one fused multiply-add per element); lane l
 //             of one wavefront sums p_c for c = l, l+64, ... in order; then a
 //             xor butterfly (32, 16, 8, 4, 2, 1); lane 0's value
 //   RMSNorm   x = round((h' * (sumsq/d + eps)^-1/2) * gamma)
@@ -62,7 +63,7 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
       unpack(wv, w, T());
       unpack(ld16(xr + c * VN), x, T());
 #pragma unroll
-      for (int j = 0; j < VN; ++j) acc += x[j] * w[j];
+      for (int j = 0; j < VN; ++j) acc = __builtin_fmaf(x[j], w[j], acc);
     };
 #pragma unroll
     for (int i = 0; i < kRouterChunks; ++i)
@@ -224,14 +225,14 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
     } else {
       unpack8(ld8(hrow), h, T());
     }
-    float p = 0.f;
+    float p = h[0] * h[0];
 #pragma unroll
-    for (int i = 0; i < HV; ++i) p += h[i] * h[i];
+    for (int i = 1; i < HV; ++i) p = __builtin_fmaf(h[i], h[i], p);
     const float lower = __shfl_xor(p, 1);
     if (half) {
       p = lower;
 #pragma unroll
-      for (int i = 0; i < HV; ++i) p += h[i] * h[i];
+      for (int i = 0; i < HV; ++i) p = __builtin_fmaf(h[i], h[i], p);
       pl[r * nvec + ch] = p;
     }
     const uint2 pk = pack8(h, T());
@@ -295,7 +296,11 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
 // once they have completed, the block adds 1 to every copy of the routing
 // counter (done[i * stride], i < copies).  Group 0 also writes h_dst, which
 // only later launches read.
-template <typename T>
+// kInLaunch: h_src and the slots were written by other blocks of the same
+// launch (agent-scope loads) and h_dst is read by later blocks of it
+// (write-through).  kFinal: route_block's kFinal mode (final norm, x_f to
+// a.x_out, argkey[t] cleared), no router.
+template <typename T, bool kInLaunch = false, bool kFinal = false>
 __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int eg, unsigned char *smem,
                             unsigned *done, int copies, int stride) {
   constexpr int VN = Vec<T>::N;
@@ -308,8 +313,16 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
   float *inv = reinterpret_cast<float *>(smem + L.inv);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e_blk = kRouteGroup * eg;
-  const bool router_wave = 4 * wv < kRouteGroup && e_blk + 4 * wv < a.E;
+  const bool router_wave = !kFinal && 4 * wv < kRouteGroup && e_blk + 4 * wv < a.E;
   const bool writer = eg == 0;
+  auto slot4 = [](const float *p, float *o) {
+    if constexpr (kInLaunch) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      ld_f32<4>(p, o);
+    }
+  };
 
   uint4 wq[kRouterChunks];
   if (router_wave) router_preload<T>(wq, static_cast<const T *>(a.router_w), a.E, e_blk + 4 * wv, d);
@@ -324,8 +337,8 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
 #pragma unroll
       for (int s = 0; s < kSlotBatch; ++s)
 #pragma unroll
-        for (int i = 0; i < VN; i += 4) ld_f32<4>(sp + static_cast<size_t>(min(s, a.nslot - 1)) * d + i, v[s] + i);
-      const uint4 hq = ld16(hrow);
+        for (int i = 0; i < VN; i += 4) slot4(sp + static_cast<size_t>(min(s, a.nslot - 1)) * d + i, v[s] + i);
+      const uint4 hq = kInLaunch ? ld16_agent(hrow) : ld16(hrow);
 #pragma unroll
       for (int i = 0; i < VN; ++i) y[i] = 0.f + v[0][i];
 #pragma unroll
@@ -337,7 +350,7 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
         for (int s = 0; s < kSlotBatch; ++s)
 #pragma unroll
           for (int i = 0; i < VN; i += 4)
-            ld_f32<4>(sp + static_cast<size_t>(min(s0 + s, a.nslot - 1)) * d + i, v[s] + i);
+            slot4(sp + static_cast<size_t>(min(s0 + s, a.nslot - 1)) * d + i, v[s] + i);
 #pragma unroll
         for (int s = 0; s < kSlotBatch; ++s)
 #pragma unroll
@@ -347,16 +360,20 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
 #pragma unroll
       for (int i = 0; i < VN; ++i) h[i] = round_to<T>(h[i] + y[i]);
     } else {
-      unpack(ld16(hrow), h, T());
+      unpack(kInLaunch ? ld16_agent(hrow) : ld16(hrow), h, T());
     }
-    float p = 0.f;
+    float p = h[0] * h[0];
 #pragma unroll
-    for (int i = 0; i < VN; ++i) p += h[i] * h[i];
+    for (int i = 1; i < VN; ++i) p = __builtin_fmaf(h[i], h[i], p);
     pl[ch] = p;
     const uint4 pk = pack(h, T());
     st16(hl + ch * VN, pk);
     st16(gl + ch * VN, gv);
-    if (c.slots && c.h_dst && writer) st16(static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + ch * VN, pk);
+    if (c.slots && c.h_dst && writer) {
+      T *hd = static_cast<T *>(c.h_dst) + static_cast<size_t>(t) * d + ch * VN;
+      if constexpr (kInLaunch) st16_through(hd, pk);
+      else st16(hd, pk);
+    }
   }
   __syncthreads();
   if (wv == 0) {  // sum of squares and 1/rms, in route_block's order
@@ -385,10 +402,14 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
       __hip_atomic_store(q + 3, pk.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __syncthreads();
-  if (router_wave)
-    router_rows<T, true>(wq, hl, 0, 1, d, static_cast<const T *>(a.router_w), a.router_b, a.E, e_blk + 4 * wv,
-                         a.logits + static_cast<size_t>(t) * 64);
+  if constexpr (kFinal) {
+    if (tid == 0) __hip_atomic_store(a.argkey + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    __syncthreads();
+    if (router_wave)
+      router_rows<T, true>(wq, hl, 0, 1, d, static_cast<const T *>(a.router_w), a.router_b, a.E, e_blk + 4 * wv,
+                           a.logits + static_cast<size_t>(t) * 64);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's x and logits have completed
   __syncthreads();
   if (tid < copies)

@@ -233,3 +233,29 @@ def test_noalloc_verify_step_rejects_bad_arguments(lib):
     assert call(B=64) == bd.MV_ERR_WORKSPACE
     assert "16 MiB" in bd.mv_last_error()
     assert call(B=0, h_in=None, argmax=None) == bd.MV_OK
+
+
+def test_one_launch_verify_step_rejects_bad_arguments(lib):
+    """The one-launch step takes batches of at most 8 rows and 16 layers; it
+    validates like moe_verify_step before anything is enqueued."""
+    cfg, w = _cfg(), _weights()
+
+    def call(B=1, K=3, h_in=FAKE, argmax=FAKE, c=cfg, ws_bytes=1 << 40):
+        return lib.moe_verify_step_one_launch(ctypes.byref(c), ctypes.byref(w), B, K, h_in, FAKE, None, argmax,
+                                              FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+    assert call(h_in=None) == bd.MV_ERR_NULL
+    assert call(K=16) == bd.MV_ERR_SHAPE
+    assert call(ws_bytes=1024) == bd.MV_ERR_WORKSPACE
+    assert call(B=3, K=3) == bd.MV_ERR_UNSUPPORTED  # 12 rows
+    assert "8 rows" in bd.mv_last_error()
+    assert call(c=_cfg(n_layers=17)) == bd.MV_ERR_UNSUPPORTED
+    assert call(B=0, h_in=None, argmax=None) == bd.MV_OK
+
+
+def test_one_launch_workspace_holds_its_counters(lib):
+    """Batches of up to 8 rows reserve the one-launch step's counter lines
+    (one set per layer) and argument block; larger batches do not."""
+    c = _cfg()
+    per_row = bd.mv_workspace_bytes(c, 9) - bd.mv_workspace_bytes(c, 8)
+    assert per_row < 0  # the 8-row workspace carries the one-launch regions
+    assert bd.mv_workspace_bytes(c, 8) - bd.mv_workspace_bytes(c, 4) > 0

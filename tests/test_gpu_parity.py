@@ -529,3 +529,92 @@ def test_wait_timeout_is_reported(bd, torch_cuda, big, B):
     assert bd.step_status(model) == 0
     for key in ("h_out", "argmax", "topk_ids"):
         assert np.array_equal(_host(bd, again[key]), _host(bd, ref[key])), key
+
+
+# ---------------------------------------------------------------- one launch
+
+
+def _one_launch_case(bd, torch, dims, model, B, K, seed):
+    """Inputs of a one-launch comparison: drafts that accept fully in sequence 0
+    (its argmax) and random ones elsewhere, and the launches' outputs on them."""
+    T = B * (K + 1)
+    h = _dev(bd, synth.make_hidden(dims, T, seed=seed))
+    rnd = np.random.default_rng(seed).integers(0, dims.vocab, (B, K)).astype(np.int32)
+    first = bd.run_verify_step(model, h, _dev(bd, rnd), B, K)
+    _sync(torch)
+    g = _host(bd, first["argmax"]).reshape(B, K + 1)
+    rnd[0] = g[0, :K]
+    drafts = _dev(bd, rnd)
+    ref = bd.run_verify_step(model, h, drafts, B, K, routing=True)
+    _sync(torch)
+    return h, drafts, {k: _host(bd, v) for k, v in ref.items() if v is not None}
+
+
+@pytest.mark.parametrize("model_name,B,K", [("big", 1, 0), ("big", 1, 3), ("big", 2, 1), ("big", 2, 3),
+                                            ("tiny", 1, 3), ("tiny", 2, 3), ("tiny3", 1, 1), ("tiny3", 2, 3)])
+def test_one_launch_step_equals_the_launches(bd, torch_cuda, tiny, tiny3, big, model_name, B, K):
+    """moe_verify_step_one_launch runs the launches' blocks as virtual blocks
+    of one launch with the same arithmetic: every output equals
+    moe_verify_step's bit for bit, twice in a row on one workspace (the setup
+    kernel clears what the first call left), and no wait gave up."""
+    torch = torch_cuda
+    dims, W, model = {"tiny": tiny, "tiny3": tiny3, "big": big}[model_name]
+    h, drafts, ref = _one_launch_case(bd, torch, dims, model, B, K, seed=900 + 10 * B + K)
+    if K:
+        assert ref["n_committed"][0] == K + 1  # sequence 0 takes the bonus token
+    for rep in range(2):
+        out = bd.run_verify_step(model, h, drafts, B, K, routing=True, one_launch=True)
+        _sync(torch)
+        assert bd.step_status(model) == 0
+        for key, want in ref.items():
+            assert np.array_equal(_host(bd, out[key]), want), (rep, key)
+
+
+@pytest.mark.parametrize("model_name", ["tiny3", "big"])
+def test_one_launch_step_in_place_and_shrinking(bd, torch_cuda, tiny3, big, model_name):
+    """h_out aliasing h_in (the combines keep reading buffers other than the
+    one they write), then a smaller batch on the same workspace: both equal
+    the launches bit for bit."""
+    torch = torch_cuda
+    dims, W, model = {"tiny3": tiny3, "big": big}[model_name]
+    for B, K in ((2, 3), (1, 1)):
+        h, drafts, ref = _one_launch_case(bd, torch, dims, model, B, K, seed=950 + B)
+        ht = h.clone()
+        T = B * (K + 1)
+        out = {"argmax": torch.empty(T, dtype=torch.int32, device="cuda"),
+               "n_accepted": torch.empty(B, dtype=torch.int32, device="cuda"),
+               "committed": torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
+               "n_committed": torch.empty(B, dtype=torch.int32, device="cuda"),
+               "topk_ids": torch.empty((dims.n_layers, T, dims.top_k), dtype=torch.int32, device="cuda")}
+        bd.moe_verify_step_one_launch(model.cfg, model.weights, B, K, ht, drafts, ht, out["argmax"],
+                                      out["n_accepted"], out["committed"], out["n_committed"], out["topk_ids"],
+                                      model.ws, model.ws_bytes)
+        _sync(torch)
+        assert bd.step_status(model) == 0
+        assert np.array_equal(_host(bd, ht), ref["h_out"]), (B, K)
+        for key, v in out.items():
+            assert np.array_equal(_host(bd, v), ref[key]), (B, K, key)
+
+
+def test_one_launch_wait_timeout_is_reported(bd, torch_cuda, big):
+    """The one-launch step's waits are bounded like the fused launch's: with
+    the bound set to zero polls from the host the kernel still runs to its end
+    and the status word reads 1; the next call with the default bound reads 0
+    and gives the launches' results again."""
+    torch = torch_cuda
+    dims, W, model = big
+    B, K = 1, 3
+    h, drafts, ref = _one_launch_case(bd, torch, dims, model, B, K, seed=970)
+    prev = bd.mv_set_spin_limit(0)
+    try:
+        bd.run_verify_step(model, h, drafts, B, K, routing=True, one_launch=True)
+        _sync(torch)
+        forced = bd.step_status(model)
+    finally:
+        bd.mv_set_spin_limit(prev)
+    assert forced == 1
+    again = bd.run_verify_step(model, h, drafts, B, K, routing=True, one_launch=True)
+    _sync(torch)
+    assert bd.step_status(model) == 0
+    for key, want in ref.items():
+        assert np.array_equal(_host(bd, again[key]), want), key
