@@ -25,6 +25,7 @@ constexpr int kUnrollFused = 20;  // the same in the fused small-batch launch (f
 
 struct TileInfo {
   int e, r0, m;
+  int j = 0;  // the tile's index among its expert's tiles
 };
 
 template <typename T>

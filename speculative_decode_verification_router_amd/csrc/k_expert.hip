@@ -114,6 +114,7 @@ __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo 
     ti.e = e;
     ti.r0 = __builtin_amdgcn_readlane(seg_e, e) + j * kTileM;
     ti.m = min(kTileM, __builtin_amdgcn_readlane(c, e) - j * kTileM);
+    ti.j = j;
     int run = 0;  // pairs of expert e before this batch of 64
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -129,6 +130,7 @@ __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo 
     ti.e = E + s;
     ti.r0 = np + s * T + j * kTileM;
     ti.m = min(kTileM, T - j * kTileM);
+    ti.j = j;
     if (lane < ti.m) rows[lane] = (j * kTileM + lane) * p.nslot + k + s;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -150,8 +152,16 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(ExpertArgs p) {
   if (small ? !small_tile<kIdLoads>(p, p.ids, blockIdx.y, ti, st, first && threadIdx.x < kWave)
             : !table_tile(p, blockIdx.y, ti))
     return;
+  // Slot pair of this block.  Blocks go to the eight XCDs round-robin in
+  // launch order, so with gridDim.x slot pairs per tile, slot pair x of an
+  // expert's tile j would land on an XCD shifted by gridDim.x * j (mod 8)
+  // from its first tile's, and read the same weight slice through another
+  // L2.  Rotating the slot pairs by that shift keeps every slice of an
+  // expert on one XCD (but the few that wrap).
+  const int shift = small ? static_cast<int>((gridDim.x * ti.j) & 7u) : 0;
+  const int pair = (static_cast<int>(blockIdx.x) + shift) % static_cast<int>(gridDim.x);
   GateUpPart<T, U, true> part;  // two weight batches in flight (the x tile's LDS, not registers, bounds occupancy)
-  part.begin(p, ti, blockIdx.x, threadIdx.x);  // first weights in flight while x is staged
+  part.begin(p, ti, pair, threadIdx.x);  // first weights in flight while x is staged
 
   const int d = p.d, nvec = d / VN, lda = d + VN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
