@@ -163,6 +163,41 @@ def test_layer_forward_tiny_fp32(bd, torch_cuda, tiny, T):
     _layer_check(bd, torch_cuda, dims, W, model, 0, h, f"tiny T={T}")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("model_name,layer", [("tiny", 0), ("big", 6)])
+def test_layer_forward_maximum_batch(bd, torch_cuda, tiny, big, model_name, layer):
+    """The largest batch the library takes, 65,535 rows, through one layer:
+    at full width the GEMM path with a ragged last tile (65,535 = 255 x 256 +
+    255) after the large-batch routing and counting-sort grouping; in fp32 the
+    64-row tiles.  256 sampled rows (the first and the last among them)
+    against the oracle, single-layer near-tie rule."""
+    torch = torch_cuda
+    dims, W, model = {"tiny": tiny, "big": big}[model_name]
+    T = 65535
+    ws_bytes = bd.mv_workspace_bytes(model.cfg, T)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    h = synth.make_hidden(dims, T, seed=65535)
+    ht = _dev(bd, h)
+    out = {"h_out": torch.empty_like(ht),
+           "topk_ids": torch.empty((T, dims.top_k), dtype=torch.int32, device="cuda"),
+           "topk_w": torch.empty((T, dims.top_k), dtype=torch.float32, device="cuda"),
+           "y_moe": torch.empty((T, dims.d_model), dtype=torch.float32, device="cuda")}
+    bd.moe_layer_forward(model.cfg, model.weights, layer, T, ht, out["h_out"], out["topk_ids"], out["topk_w"],
+                         out["y_moe"], ws, ws_bytes)
+    _sync(torch)
+    sample = np.sort(np.random.default_rng(7).choice(np.arange(1, T - 1), 254, replace=False))
+    sample = np.concatenate([[0], sample, [T - 1]])
+    ref = O.moe_layer(O.widen(h[sample], dims.dtype), W, layer, dims)
+    tally = Tally(len(sample), forced=True)
+    tally.routing(layer, _host(bd, out["topk_ids"])[sample], ref["ids"], ref["margin"])
+    tol = TOL[dims.dtype]
+    tally.rows(f"max batch {model_name} y_moe", _host(bd, out["y_moe"])[sample], ref["y"], tol)
+    tally.rows(f"max batch {model_name} h_out", O.widen(_host(bd, out["h_out"]), dims.dtype)[sample],
+               ref["h_out"], tol)
+    tally.assert_ok(f"{model_name}: 65,535 rows, 256 sampled")
+    del ws
+
+
 # 128 / 129 and 512 / 513 sit on either side of a batch-path switch (16-row
 # tiles, 64-row tiles, 256-row GEMM tiles); 513 leaves the GEMM a one-row tile.
 @pytest.mark.parametrize("T,layer", [(4, 0), (37, 11), (128, 5), (129, 2), (200, 3), (512, 4), (513, 9),
