@@ -108,7 +108,8 @@ Layout layout(const mv_config &c, int T) {
   L.argkey = take(static_cast<size_t>(T) * 8);
   L.done = take(4);
   L.bcnt = take(static_cast<size_t>(mv::route_large_blocks(T)) * 64 * 4);
-  L.logits = take(static_cast<size_t>(T) * 64 * 4);
+  // router logits of the batches routed to logits, one buffer per layer parity
+  L.logits = take(2 * static_cast<size_t>(T) * 64 * 4);
   // two sets of fused-launch counters (tiles, then the routing copies)
   L.tdone = take(2 * done_set_words(c, T) * 4);
   // the one-launch step (batches routed to logits): its counters and arguments
@@ -231,7 +232,11 @@ struct Step {
   bool small() const { return T <= mv::kSmallT; }
   // Router logits spread over expert groups, top-k in the gate/up kernel.
   bool logits_route() const { return T <= mv::kLogitsMaxT; }
-  float *logits() const { return reinterpret_cast<float *>(ws + L.logits); }
+  // logits buffer of the layers of parity `par` (the fused launch of a
+  // layer fills the next one's with kLogitUnset before that layer routes)
+  float *logits(int par = 0) const {
+    return reinterpret_cast<float *>(ws + L.logits) + static_cast<size_t>(par & 1) * T * 64;
+  }
   // fused-launch counter set s (0 or 1): tile counters, then the routing copies
   unsigned *done_set(int s) const {
     return reinterpret_cast<unsigned *>(ws + L.tdone) + static_cast<size_t>(s) * done_set_words(c, T);
@@ -282,7 +287,11 @@ struct Step {
     const LayerPtrs lp = layer_ptrs(c, w, layer);
     mv::ExpertArgs e = expert_args(layer, ids, gates, logits);
     const int mt = max_tiles(c, T);
-    if (logits) return hip_status(mv::launch_ffn_small(c.dtype, e, ra, ca, mt, s));
+    if (logits) {
+      e.logits = this->logits(layer);
+      e.logits_next = this->logits(layer + 1);
+      return hip_status(mv::launch_ffn_small(c.dtype, e, ra, ca, mt, s));
+    }
     const Path path = path_for(c, T);
     int rc = hip_status(path == kGemmTiles  ? mv::launch_gemm_gate_up(e, mt, s)
                         : path == kMidTiles ? mv::launch_gate_up_mid(c.dtype, e, mt, s)
@@ -436,7 +445,7 @@ int verify_launches(const mv_config *cfg, const mv_weights *w, int32_t B, int32_
     if (lg) {
       mv::RouteArgs ra = st.route_args(layer, mv::kRoute, ids, gates);
       ra.mode = mv::kLogits;
-      ra.logits = st.logits();
+      ra.logits = st.logits(layer);
       const mv::CombineArgs cb{cur, dst, st.slots(), nullptr};
       rc = st.ffn(layer, ids, gates, nullptr, nullptr, nullptr, true, &ra, &cb);
     } else if (!(rc = st.route(layer, mv::kRoute, cur, dst, st.slots(), nullptr, ids, gates))) {

@@ -64,6 +64,34 @@ __device__ void small_top_k(const ExpertArgs &p, SmallTiles &st, bool write_reco
     }
 }
 
+// Wavefront w reads the logits of rows w, w+4, ... (agent-scope loads) until
+// none of the first E holds kLogitUnset, at most spin_limit polls (a wait
+// that gives up records 1 in *err and goes on); with `select` it then takes
+// their top-k as small_top_k does.  Synchronises the block.
+__device__ void small_top_k_poll(const ExpertArgs &p, SmallTiles &st, bool select, bool write_record) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1), k = p.k;
+  for (int t = w; t < p.T; t += kThreads / kWave) {
+    const float *row = p.logits + static_cast<size_t>(t) * 64 + lane;
+    float v = 0.f;
+    for (int polls = 0;; ++polls) {
+      v = __hip_atomic_load(row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!__ballot(lane < p.E && __float_as_uint(v) == kLogitUnset)) break;
+      if (polls >= p.spin_limit) {
+        if (lane == 0) __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(64);
+    }
+    if (select) select_top_k_of(v, st.keys[w], st.sel[w], p.E, k, st.ids + t * k, st.gates + t * k);
+  }
+  __syncthreads();
+  if (select && write_record && w == 0)
+    for (int i = lane; i < p.T * k; i += kWave) {
+      p.ids_out[i] = st.ids[i];
+      p.gates_out[i] = st.gates[i];
+    }
+}
+
 // routed_only: y counts routed tiles only.  NL: id loads per lane (T*k <= 64*NL).
 template <int NL>
 __device__ bool small_tile(const ExpertArgs &p, const int *ids, int y, TileInfo &ti, SmallTiles &st,
@@ -241,8 +269,11 @@ __device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const 
                                 int n_route, int vb, unsigned char *smem, SmallTiles &st, float (*xacc)[64][4]) {
   constexpr int VN = Vec<T>::N;
   const int d = p.d, F = p.F, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (vb == 0)  // the next launch's counters (this launch's were cleared before it started)
+  if (vb == 0) {  // the next launch's counters (this launch's were cleared before it started) and logits
     for (int i = tid; i < p.n_done; i += blockDim.x) p.done_next[static_cast<size_t>(i) * kDoneStride] = 0u;
+    if (p.logits_next)
+      for (int i = tid; i < p.T * 64; i += blockDim.x) p.logits_next[i] = __uint_as_float(kLogitUnset);
+  }
   if (vb < n_route) {
     const int G = (p.E + kRouteGroup - 1) / kRouteGroup;
     route_fused<T, kInLaunch>(ra, ca, vb / G, vb % G, smem, p.route_done, kRouteCopies, kDoneStride);
@@ -269,12 +300,16 @@ __device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   } else {
-    if (n_route) {
-      wait_count(route_ctr, n_route, p.err, p.spin_limit);
-      __syncthreads();
-    }
     const bool record = gu && y == n_sh && pair == 0;  // writes ids and gates of record
-    small_top_k(p, st, record);
+    if (n_route && !kInLaunch) {
+      small_top_k_poll(p, st, true, record);
+    } else {
+      if (n_route) {
+        wait_count(route_ctr, n_route, p.err, p.spin_limit);
+        __syncthreads();
+      }
+      small_top_k(p, st, record);
+    }
     if (!small_tile<kIdLoadsLogits>(p, st.ids, y - n_sh, ti, st, false, true)) return;
   }
   // LDS tile: rows [0, R) hold the tile's rows (R = min(T, 16) >= m), row R
@@ -287,8 +322,12 @@ __device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const 
     GateUpPart<T, kUnrollFused> part;
     part.begin(p, ti, pair, tid);
     if (shared && n_route) {  // x is written by this launch's routing blocks
-      wait_count(route_ctr, n_route, p.err, p.spin_limit);
-      __syncthreads();
+      if constexpr (kInLaunch) {
+        wait_count(route_ctr, n_route, p.err, p.spin_limit);
+        __syncthreads();
+      } else {
+        small_top_k_poll(p, st, false, false);  // a row's logits land after its x
+      }
     }
     const int nvec = d / VN, lda = d + VN;
     const T *x = static_cast<const T *>(p.x);

@@ -47,6 +47,11 @@ constexpr int kRouteCopies = 32;
 // Polls (about a microsecond each) a fused-launch wait makes before it gives
 // up and records the timeout in the call's status word.
 constexpr int kSpinLimitDefault = 1 << 18;
+// Bit pattern of a router logit not yet written: a negative NaN with every
+// payload bit set, which the routing arithmetic does not produce unless an
+// input holds it.  A fused launch that routes its own layer reads the logits
+// as they land; the launch before it fills their buffer with this pattern.
+constexpr uint32_t kLogitUnset = 0xffffffffu;
 
 struct RouteArgs {
   int T, d, E, S, k, nslot, mode;
@@ -104,6 +109,9 @@ struct ExpertArgs {
   int n_done;
   unsigned *err;           // the call's status word: set to 1 if a fused launch's wait gave up
   int spin_limit;          // polls before a fused launch's wait gives up
+  // fused launch: the next layer's logits buffer ([T, 64]), which block 0
+  // fills with kLogitUnset (null: none)
+  float *logits_next;
 };
 
 struct AcceptArgs {

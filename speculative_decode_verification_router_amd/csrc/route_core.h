@@ -42,6 +42,33 @@ __device__ __forceinline__ void router_preload(uint4 *wq, const T *w_router, int
     if (q + 16 * i < nvec) wq[i] = ld16(wr + (q + 16 * i) * VN);
 }
 
+// Router logit (without bias) of expert e_base + lane / 16 for the x row at
+// xr (LDS), the same value in all 16 lanes of the expert.
+template <typename T>
+__device__ __forceinline__ float router_dot(const uint4 *wq, const T *xr, int d, const T *w_router, int E,
+                                            int e_base) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63, q = lane & 15;
+  const int e = e_base + (lane >> 4);
+  const int nvec = d / VN;
+  const T *wr = w_router + static_cast<size_t>(min(e, E - 1)) * d;
+  float acc = 0.f;
+  auto accumulate = [&](const uint4 &wv, int c) {
+    float w[VN], x[VN];
+    unpack(wv, w, T());
+    unpack(ld16(xr + c * VN), x, T());
+#pragma unroll
+    for (int j = 0; j < VN; ++j) acc = __builtin_fmaf(x[j], w[j], acc);
+  };
+#pragma unroll
+  for (int i = 0; i < kRouterChunks; ++i)
+    if (q + 16 * i < nvec) accumulate(wq[i], q + 16 * i);
+  for (int c = q + 16 * kRouterChunks; c < nvec; c += 16) accumulate(ld16(wr + c * VN), c);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+  return acc;
+}
+
 // Router logits of tokens [0, nt) of the x rows in LDS (x_lds[t*ldx + j]).
 // kThrough: the logits are written through (read by other blocks of the
 // same launch).
@@ -49,28 +76,11 @@ template <typename T, bool kThrough = false>
 __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int ldx, int nt, int d,
                                             const T *w_router, const float *bias, int E, int e_base,
                                             float *lg) {
-  constexpr int VN = Vec<T>::N;
   const int lane = threadIdx.x & 63, q = lane & 15;
   const int e = e_base + (lane >> 4);
-  const int nvec = d / VN;
-  const T *wr = w_router + static_cast<size_t>(min(e, E - 1)) * d;
   const float b = (bias && e < E) ? bias[e] : 0.f;
   for (int t = 0; t < nt; ++t) {
-    const T *xr = x_lds + t * ldx;
-    float acc = 0.f;
-    auto accumulate = [&](const uint4 &wv, int c) {
-      float w[VN], x[VN];
-      unpack(wv, w, T());
-      unpack(ld16(xr + c * VN), x, T());
-#pragma unroll
-      for (int j = 0; j < VN; ++j) acc = __builtin_fmaf(x[j], w[j], acc);
-    };
-#pragma unroll
-    for (int i = 0; i < kRouterChunks; ++i)
-      if (q + 16 * i < nvec) accumulate(wq[i], q + 16 * i);
-    for (int c = q + 16 * kRouterChunks; c < nvec; c += 16) accumulate(ld16(wr + c * VN), c);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+    const float acc = router_dot<T>(wq, x_lds + t * ldx, d, w_router, E, e_base);
     if (q == 0 && e < 64) {
       if constexpr (kThrough) __hip_atomic_store(lg + t * 64 + e, acc + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else lg[t * 64 + e] = acc + b;
@@ -78,20 +88,16 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
   }
 }
 
-// Top-k of one token's logits lg_row[0..E) on one wavefront: lane e's rank
+// Top-k of one token's logits on one wavefront: lane e's rank
 // is the number of experts ordered before it by (logit desc, id asc).  Each
 // lane's (logit, id) key goes to LDS once (lanes >= E write 0, below every
 // real key) and every lane counts the keys above its own, two per read.
-// key_lds: 64 keys, 16-byte aligned; sel_lds: kMaxTopK floats.  kCoherent:
-// the logits were written by other blocks of the same launch and are read
-// with agent-scope loads.  cnt_lds (LDS, optional): 1 is added to the count
-// of every chosen expert.
-template <bool kCoherent = false>
-__device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_lds, float *sel_lds, int E,
-                                             int k, int *ids, float *gates, int *cnt_lds = nullptr) {
+// key_lds: 64 keys, 16-byte aligned; sel_lds: kMaxTopK floats.  logit: lane
+// e's logit (lanes >= E: any value).  cnt_lds (LDS, optional): 1 is added to
+// the count of every chosen expert.
+__device__ __forceinline__ void select_top_k_of(float logit, uint64_t *key_lds, float *sel_lds, int E, int k,
+                                                int *ids, float *gates, int *cnt_lds = nullptr) {
   const int lane = threadIdx.x & 63;
-  const float logit = kCoherent ? __hip_atomic_load(lg_row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : lg_row[lane];
   const uint64_t mine = lane < E ? argmax_key(logit, static_cast<uint32_t>(lane)) : 0ull;
   key_lds[lane] = mine;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -125,6 +131,17 @@ __device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_
 #pragma unroll
   for (int s = 1; s < kMaxTopK; ++s) den += s < k ? v[s] : -0.f;
   if (chosen) gates[rank] = ex / den;
+}
+
+// select_top_k_of on lg_row[0..64).  kCoherent: the logits were written by
+// other blocks of the same launch and are read with agent-scope loads.
+template <bool kCoherent = false>
+__device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_lds, float *sel_lds, int E,
+                                             int k, int *ids, float *gates, int *cnt_lds = nullptr) {
+  const int lane = threadIdx.x & 63;
+  const float logit = kCoherent ? __hip_atomic_load(lg_row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : lg_row[lane];
+  select_top_k_of(logit, key_lds, sel_lds, E, k, ids, gates, cnt_lds);
 }
 
 // LDS layout of a routing block holding `ntok` token rows.
@@ -292,10 +309,13 @@ __device__ void route_block(const RouteArgs &a, const CombineArgs &c, int t0, in
 // 256 threads takes token t's combine and RMSNorm and the logits of expert
 // group eg.  The arithmetic is route_block's in kLogits mode, with one thread
 // per 16-byte chunk (its sum of squares is the same sequential sum).  x and
-// the logits, which other blocks of the launch read, are written through;
-// once they have completed, the block adds 1 to every copy of the routing
-// counter (done[i * stride], i < copies).  Group 0 also writes h_dst, which
-// only later launches read.
+// the logits, which other blocks of the launch read, are written through.
+// In the fused expert launch the logits are stored once x has completed, and
+// the readers take them as they land (their buffer was filled with
+// kLogitUnset before the launch).  In the one-launch step (kInLaunch), once x
+// and the logits have completed the block adds 1 to every copy of the
+// routing counter (done[i * stride], i < copies).  Group 0 also writes h_dst,
+// which only later launches read.
 // kInLaunch: h_src and the slots were written by other blocks of the same
 // launch (agent-scope loads) and h_dst is read by later blocks of it
 // (write-through).  kFinal: route_block's kFinal mode (final norm, x_f to
@@ -404,6 +424,22 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
   }
   if constexpr (kFinal) {
     if (tid == 0) __hip_atomic_store(a.argkey + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if constexpr (!kInLaunch) {
+    // the fused launch's readers take the logits as they land, so x must
+    // have completed before any logit is stored; the wait overlaps the
+    // router's dot products
+    __syncthreads();
+    const int e = e_blk + 4 * wv + (lane >> 4);
+    float lg = 0.f;
+    if (router_wave) {
+      lg = router_dot<T>(wq, hl, d, static_cast<const T *>(a.router_w), a.E, e_blk + 4 * wv);
+      lg += (a.router_b && e < a.E) ? a.router_b[e] : 0.f;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's x has completed
+    __syncthreads();
+    if (router_wave && (lane & 15) == 0 && e < 64)
+      __hip_atomic_store(a.logits + static_cast<size_t>(t) * 64 + e, lg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   } else {
     __syncthreads();
     if (router_wave)
