@@ -27,9 +27,9 @@ METRIC = "committed tokens/s (12-layer MoE verify, K=3) + % of HBM/MFMA roofline
 # measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by a 1 GiB copy;
 # profiles/verify_step_{b1,c32}_k3_hbm_counters.txt, profiles/mtp_draft_b1_k3_hbm_counters.txt)
 # on the kernel sources with this digest; reported only while the sources match.
-MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "ba0154d6e54fc800", "bytes_per_step": 2.1848e9},
-                    "c32_k3": {"csrc_sha256_16": "ba0154d6e54fc800", "bytes_per_step": 6.4058e9},
-                    "b1_k3_draft": {"csrc_sha256_16": "ba0154d6e54fc800", "bytes_per_step": 1.0573e9}}
+MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "598528188fdfb3d7", "bytes_per_step": 2.1846e9},
+                    "c32_k3": {"csrc_sha256_16": "598528188fdfb3d7", "bytes_per_step": 6.4054e9},
+                    "b1_k3_draft": {"csrc_sha256_16": "598528188fdfb3d7", "bytes_per_step": 1.0573e9}}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
