@@ -74,6 +74,24 @@ def tiny3(bd):
     return dims, W, _model(bd, dims, W, 64)
 
 
+# Other model shapes the library takes: fewer routed experts (the routing's
+# expert groups, the top-k lanes and the tile search past E), one or three
+# shared experts, top-k of 4, 5 and 8, several layers.  odd16g fits the
+# large-batch GEMM path (d % 256 == 0, d_ff % 128 == 0, at most 2 shared).
+ODD_F32 = synth.ModelDims(128, 64, 20, 1, 4, 3, 300, 1e-6, "f32")
+ODD_BF16 = synth.ModelDims(256, 192, 40, 3, 8, 2, 5000, 1e-6, "bf16")
+ODD_BF16_GEMM = synth.ModelDims(256, 256, 24, 2, 5, 2, 3000, 1e-6, "bf16")
+
+
+@pytest.fixture(scope="module")
+def odd(bd):
+    out = {}
+    for name, dims, sigma in (("odd32", ODD_F32, None), ("odd16", ODD_BF16, 0.05), ("odd16g", ODD_BF16_GEMM, 0.05)):
+        W = synth.make_weights(dims, seed=11, sigma=sigma, gamma="uniform")
+        out[name] = (dims, W, _model(bd, dims, W, 700))
+    return out
+
+
 def _dev(bd, a):
     return bd.to_device(a)
 
@@ -420,6 +438,58 @@ def test_router_bias_zipf(bd, torch_cuda, big):
     modelz = model.with_router_bias(Wz["router_b"])
     h = synth.make_hidden(dims, 8 * 4, seed=55)
     _forced_check(bd, torch_cuda, dims, Wz, modelz, h, 8, 3, 0.6, 9, "zipf bias verify")
+
+
+# ---------------------------------------------------------------- other shapes
+
+
+@pytest.mark.parametrize("name,T", [("odd32", 4), ("odd32", 100), ("odd32", 300), ("odd16", 4), ("odd16", 100),
+                                    ("odd16", 300), ("odd16g", 600)])
+def test_layer_forward_other_shapes(bd, torch_cuda, odd, name, T):
+    """One layer of each odd shape on the 16-row, 64-row and (odd16g, 600
+    rows) GEMM paths against the oracle."""
+    dims, W, model = odd[name]
+    h = synth.make_hidden(dims, T, seed=500 + T)
+    _layer_check(bd, torch_cuda, dims, W, model, dims.n_layers - 1, h, f"{name} T={T}")
+
+
+@pytest.mark.parametrize("name,B", [("odd32", 1), ("odd32", 2), ("odd32", 8), ("odd32", 40), ("odd16", 1),
+                                    ("odd16", 2), ("odd16", 8), ("odd16", 40)])
+def test_verify_other_shapes(bd, torch_cuda, odd, name, B):
+    """Verify steps of the odd shapes (B = 1, 2: routing inside the fused
+    launch; 8: 16-row tiles; 40: 64-row tiles) against the oracle."""
+    dims, W, model = odd[name]
+    K = 3
+    h = synth.make_hidden(dims, B * (K + 1), seed=600 + B)
+    _verify_check(bd, torch_cuda, dims, W, model, h, B, K, 0.6, 7, f"{name} verify B={B}")
+
+
+@pytest.mark.parametrize("name", ["odd32", "odd16"])
+def test_other_shapes_same_results_on_every_batch_path(bd, torch_cuda, odd, name):
+    """The batch-path invariance on the odd shapes, and the one-launch step
+    bit-identical to the launches at B = 1, 2."""
+    dims, W, model = odd[name]
+    K = 3
+    n_seq = 34
+    h = synth.make_hidden(dims, n_seq * (K + 1), seed=92)
+    drafts = np.random.default_rng(5).integers(0, dims.vocab, (n_seq, K)).astype(np.int32)
+    batches = (1, 2, 4, 16, 34)
+    runs = {B: bd.run_verify_step(model, _dev(bd, h[:B * (K + 1)]), _dev(bd, drafts[:B]), B, K, routing=True)
+            for B in batches}
+    ones = {B: bd.run_verify_step(model, _dev(bd, h[:B * (K + 1)]), _dev(bd, drafts[:B]), B, K, routing=True,
+                                  one_launch=True)
+            for B in (1, 2)}
+    _sync(torch_cuda)
+    ref = runs[batches[-1]]
+    for B in batches[:-1]:
+        run, T = runs[B], B * (K + 1)
+        for key in ("h_out", "argmax", "committed", "n_committed"):
+            n = B if key in ("committed", "n_committed") else T
+            assert np.array_equal(_host(bd, run[key])[:n], _host(bd, ref[key])[:n]), (B, key)
+        assert np.array_equal(_host(bd, run["topk_ids"]), _host(bd, ref["topk_ids"])[:, :T]), B
+    for B, one in ones.items():
+        for key in ("h_out", "argmax", "committed", "n_committed", "topk_ids"):
+            assert np.array_equal(_host(bd, one[key]), _host(bd, runs[B][key])), ("one launch", B, key)
 
 
 # ---------------------------------------------------------------- invariants
