@@ -26,10 +26,11 @@ METRIC = "committed tokens/s (12-layer MoE verify, K=3) + % of HBM/MFMA roofline
 # HBM bytes per b1_k3 and c32_k3 verify step and per b1_k3 mtp_draft call,
 # measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by a 1 GiB copy;
 # profiles/verify_step_{b1,c32}_k3_hbm_counters.txt, profiles/mtp_draft_b1_k3_hbm_counters.txt)
-# on the kernel sources with this digest; reported only while the sources match.
-MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "598528188fdfb3d7", "bytes_per_step": 2.1846e9},
-                    "c32_k3": {"csrc_sha256_16": "598528188fdfb3d7", "bytes_per_step": 6.4054e9},
-                    "b1_k3_draft": {"csrc_sha256_16": "598528188fdfb3d7", "bytes_per_step": 1.0573e9}}
+# on the kernel sources whose code (comments aside) has this digest; reported
+# only while the code matches.
+MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "2fafdba49f2fc77f", "bytes_per_step": 2.1846e9},
+                    "c32_k3": {"csrc_sha256_16": "2fafdba49f2fc77f", "bytes_per_step": 6.4054e9},
+                    "b1_k3_draft": {"csrc_sha256_16": "2fafdba49f2fc77f", "bytes_per_step": 1.0573e9}}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -50,13 +51,20 @@ def step_bytes(dims, ids, T):
 
 
 def csrc_digest():
+    """Digest of the kernel sources' code: line comments, block comments and
+    blank lines are left out, so an edit of comments alone keeps it."""
     import glob
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "speculative_decode_verification_router_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

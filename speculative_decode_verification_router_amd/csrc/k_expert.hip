@@ -259,7 +259,9 @@ __device__ __forceinline__ void wait_count(const unsigned *ctr, unsigned target,
 
 // n_route > 0: the launch also routes this layer (ra, ca): its first n_route
 // blocks (token, expert group) run route_fused, and the other blocks wait
-// for them (shared gate/up blocks after requesting their first weights).
+// for them (shared gate/up blocks after requesting their first weights) by
+// reading the logits until every one has landed (the one-launch step: on
+// the routing counter).
 // Block `vb` of the launch (blockIdx.x of k_ffn_small, or a virtual block of
 // the one-launch step); kInLaunch: the one-launch step, where the routing's
 // sources were written by blocks of the same launch and the slots are read by

@@ -41,8 +41,9 @@ constexpr int kLogitsMaxT = 8;  // measured: at 16 rows separate launches are 18
 // Per-tile counters of the fused expert launch, one per 256-byte line so
 // that polls of different tiles do not meet in one memory channel.
 constexpr int kDoneStride = 64;
-// Copies of the routing counter of a fused launch that also routes, so that
-// its many waiting blocks spread their polls over that many lines.
+// Copies of a layer's routing counter in the one-launch step, so that its
+// many waiting blocks spread their polls over that many lines (the fused
+// expert launch's blocks read the logits themselves as they land).
 constexpr int kRouteCopies = 32;
 // Polls (about a microsecond each) a fused-launch wait makes before it gives
 // up and records the timeout in the call's status word.
@@ -104,7 +105,7 @@ struct ExpertArgs {
   // fused launch: this launch's counters, one per 256-byte line (cleared
   // before it starts), and the next launch's, which it clears
   unsigned *tile_done;     // [tile * kDoneStride]: gate/up blocks done per tile
-  unsigned *route_done;    // [copy * kDoneStride]: routing blocks done, kRouteCopies copies
+  unsigned *route_done;    // [copy * kDoneStride]: routing blocks done, kRouteCopies copies (one-launch step)
   unsigned *done_next;     // [i * kDoneStride], i < n_done
   int n_done;
   unsigned *err;           // the call's status word: set to 1 if a fused launch's wait gave up
