@@ -621,8 +621,8 @@ MtpLayout mtp_layout(const mv_config &c, int Fm, int B) {
     off += align256(bytes);
     return at;
   };
-  L.acc = take(b * d * 4);
-  L.acc2 = take(b * d * 4);
+  L.acc = take(mv::kMtpSplit * b * d * 4);   // K-split partials of z
+  L.acc2 = take(mv::kMtpSplit * b * d * 4);  // and of y
   L.a = take(b * static_cast<size_t>(Fm) * es);
   L.hcur = take(b * d * es);
   L.xo = take(b * d * es);

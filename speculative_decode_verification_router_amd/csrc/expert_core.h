@@ -179,23 +179,26 @@ struct GateUpPart {
 };
 
 // down of slice pair `pair` of a tile; same split as GateUpPart.  The down
-// weights are p.w_routed / p.w_shared unless given.
+// weights are p.w_routed / p.w_shared unless given.  ks / ns: this block
+// takes part ks of ns equal parts of the K windows (its two halves split
+// that part), for a partial output that the reader adds up.
 template <typename T, int U = kUnroll>
 struct DownPart {
   const T *b;
   int n0, half, slice, w_lo, w_hi;
   uint4 q[U];
   __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid,
-                                        const void *w_routed = nullptr, const void *w_shared = nullptr) {
+                                        const void *w_routed = nullptr, const void *w_shared = nullptr,
+                                        int ks = 0, int ns = 1) {
     constexpr int VN = Vec<T>::N;
     const int lane = tid & 63, wv = tid >> 6;
     slice = wv >> 1;
     half = wv & 1;
     n0 = (pair * 2 + slice) * 16;
     const int d = p.d, F = p.F, r = lane & 15, koff = (lane >> 4) * VN;
-    const int nwin = F / (4 * VN);
-    w_lo = n0 < d ? half * nwin / 2 : 0;
-    w_hi = n0 < d ? (half + 1) * nwin / 2 : 0;
+    const int nwin = F / (4 * VN), k0 = ks * nwin / ns, k1 = (ks + 1) * nwin / ns;
+    w_lo = n0 < d ? k0 + half * (k1 - k0) / 2 : 0;
+    w_hi = n0 < d ? k0 + (half + 1) * (k1 - k0) / 2 : 0;
     const T *W = w_routed ? expert_base<T>(w_routed, w_shared, p.E, ti.e, static_cast<size_t>(d) * F)
                           : expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
     b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
@@ -203,11 +206,12 @@ struct DownPart {
   }
   // tile_rows[row]: the pair id (t*nslot + slot) of tile row `row`; gates:
   // [T, k] softmax gates of the routed pairs.  kThrough: the slots are
-  // written through (read by later blocks of the same launch).
+  // written through (read by later blocks of the same launch).  out_off:
+  // offset (floats) of this block's output from p.slots.
   template <bool kThrough = false>
   __device__ __forceinline__ void finish(const ExpertArgs &p, const TileInfo &ti, const T *arow,
                                          float (*half_acc)[64][4], int tid, const int *tile_rows,
-                                         const float *gates) {
+                                         const float *gates, size_t out_off = 0) {
     const int lane = tid & 63, d = p.d;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     mfma_panel<T, U>(acc, arow, b, w_lo, w_hi, q);
@@ -224,7 +228,7 @@ struct DownPart {
         const int pair = tile_rows[row];
         const int tok = pair / p.nslot, s = pair - tok * p.nslot;
         const float w = s < p.k ? gates[tok * p.k + s] : 1.0f;
-        float *dst = p.slots + static_cast<size_t>(pair) * d + n0 + (lane & 15);
+        float *dst = p.slots + out_off + static_cast<size_t>(pair) * d + n0 + (lane & 15);
         const float v = w * (acc[i] + half_acc[slice][lane][i]);
         if constexpr (kThrough) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else *dst = v;

@@ -22,7 +22,10 @@
 // argmax keys alternate between two buffers by position parity, so a
 // projection reads the previous position's keys while its block (0, 0)
 // clears the other buffer.  The weight streams are the expert-tile parts of
-// expert_core.h with kUnrollFused windows per batch (these grids are small).
+// expert_core.h with kUnrollFused windows per batch.  The projection and the
+// FFN down split K into kMtpSplit parts, one block each (their grids are
+// small otherwise), and write fp32 partials that their readers (the FFN's
+// norm, the output kernel) add in part order.
 // A row's sum of squares is taken per 16-byte chunk in order, then over the
 // chunks as in the verify step's RMSNorm.
 #include "expert_core.h"
@@ -76,6 +79,22 @@ __device__ __forceinline__ void ld_vec(const float *p, float *v) {
   if constexpr (VN == 8) ld_f32<4>(p + 4, v + 4);
 }
 
+// VN values of a K-split output: the kMtpSplit partials at p, `stride`
+// floats apart, added in part order.
+template <int VN>
+__device__ __forceinline__ void ld_parts(const float *p, size_t stride, float *v) {
+  float q[kMtpSplit][VN];
+#pragma unroll
+  for (int s = 0; s < kMtpSplit; ++s) ld_vec<VN>(p + s * stride, q[s]);
+#pragma unroll
+  for (int i = 0; i < VN; ++i) {
+    float t = q[0][i];
+#pragma unroll
+    for (int s = 1; s < kMtpSplit; ++s) t += q[s][i];
+    v[i] = t;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_mtp_proj(ExpertArgs p, MtpArgs a, int step) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -89,7 +108,7 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_proj(ExpertArgs p, MtpArgs 
   float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(kTileM) * lda * sizeof(T));
   const TileInfo ti{0, r0, m};
   DownPart<T, kDenseU> part_w;
-  part_w.begin(p, ti, blockIdx.x, tid);  // weights in flight while u is built
+  part_w.begin(p, ti, blockIdx.x, tid, nullptr, nullptr, blockIdx.z, kMtpSplit);  // in flight while u is built
 
   const unsigned long long *key_prev = a.argkey + static_cast<size_t>((step - 1) & 1) * a.B;
   if (tid < kTileM) {
@@ -100,7 +119,7 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_proj(ExpertArgs p, MtpArgs 
       tok[tid] = min(max(t, 0), a.V - 1);
     }
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
     unsigned long long *key_cur = a.argkey + static_cast<size_t>(step & 1) * a.B;
     for (int b = tid; b < a.B; b += blockDim.x) {
       if (step > 0) a.drafts[static_cast<size_t>(b) * a.K + step - 1] = static_cast<int>(key_index(key_prev[b]));
@@ -143,7 +162,8 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_proj(ExpertArgs p, MtpArgs 
     }
   }
   __syncthreads();
-  part_w.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, half_acc, tid, rows, nullptr);
+  part_w.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, half_acc, tid, rows, nullptr,
+                static_cast<size_t>(blockIdx.z) * a.B * d);
 }
 
 template <typename T>
@@ -160,7 +180,7 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_gu(ExpertArgs p, MtpArg
   GateUpPart<T, kDenseU> part_w;
   part_w.begin(p, ti, blockIdx.x, tid);
   auto h1v = [&](int r, int ch, float *v) {  // h1 = R(z)
-    ld_vec<VN>(a.acc + static_cast<size_t>(r0 + r) * d + ch * VN, v);
+    ld_parts<VN>(a.acc + static_cast<size_t>(r0 + r) * d + ch * VN, static_cast<size_t>(a.B) * d, v);
 #pragma unroll
     for (int i = 0; i < VN; ++i) v[i] = round_to<T>(v[i]);
   };
@@ -203,12 +223,12 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_dn(ExpertArgs p, MtpArg
   const int lane = threadIdx.x & 63, r0 = blockIdx.y * kTileM;
   const TileInfo ti{0, r0, min(kTileM, a.B - r0)};
   DownPart<T, kDenseU> part_w;
-  part_w.begin(p, ti, blockIdx.x, threadIdx.x);
+  part_w.begin(p, ti, blockIdx.x, threadIdx.x, nullptr, nullptr, blockIdx.z, kMtpSplit);
   if (threadIdx.x < kTileM) rows[threadIdx.x] = r0 + threadIdx.x;
   stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
   __syncthreads();
   part_w.finish(p, ti, reinterpret_cast<const T *>(smem) + (lane & 15) * (p.F + VN) + (lane >> 4) * VN, half_acc,
-                threadIdx.x, rows, nullptr);
+                threadIdx.x, rows, nullptr, static_cast<size_t>(blockIdx.z) * a.B * a.d);
 }
 
 // Larger batches (more than kMtpFusedMaxB sequences) normalise in row
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_mid(MtpArgs a) {
   const int b = blockIdx.x, d = a.d;
   const float *z = a.acc + static_cast<size_t>(b) * d;
   auto h1v = [&](int, int ch, float *v) {
-    ld_vec<VN>(z + ch * VN, v);
+    ld_parts<VN>(z + ch * VN, static_cast<size_t>(a.B) * d, v);
 #pragma unroll
     for (int i = 0; i < VN; ++i) v[i] = round_to<T>(v[i]);
   };
@@ -311,8 +331,8 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_out(MtpArgs a, int last) {
   const float *z = a.acc + static_cast<size_t>(b) * d, *y = a.acc2 + static_cast<size_t>(b) * d;
   auto hv = [&](int, int ch, float *v) {  // h2 = R(R(z) + y)
     float q[VN];
-    ld_vec<VN>(z + ch * VN, v);
-    ld_vec<VN>(y + ch * VN, q);
+    ld_parts<VN>(z + ch * VN, static_cast<size_t>(a.B) * d, v);
+    ld_parts<VN>(y + ch * VN, static_cast<size_t>(a.B) * d, q);
 #pragma unroll
     for (int i = 0; i < VN; ++i) v[i] = round_to<T>(round_to<T>(v[i]) + q[i]);
   };
@@ -368,7 +388,8 @@ size_t mtp_ffn_lds(int d, int F, int es) {
 hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertArgs &gu, const ExpertArgs &dn,
                                const MtpArgs &a, int step, hipStream_t s) {
   const int ntiles = (a.B + kTileM - 1) / kTileM, es = dtype == 1 ? 2 : 4;
-  const dim3 g_proj((a.d + 31) / 32, ntiles), g_gu((gu.F + 31) / 32, ntiles), g_dn((a.d + 31) / 32, ntiles);
+  const dim3 g_proj((a.d + 31) / 32, ntiles, kMtpSplit), g_gu((gu.F + 31) / 32, ntiles),
+      g_dn((a.d + 31) / 32, ntiles, kMtpSplit);
   const size_t l_proj = mtp_proj_lds(a.d, es);
   const size_t l_gu = mtp_gu_lds(a.d, es);
   const size_t l_dn = static_cast<size_t>(kTileM) * (dn.F + 16 / es) * es;
