@@ -609,7 +609,7 @@ MV_API int spec_accept(int32_t B, int32_t K, const int32_t *argmax, const int32_
 namespace {
 
 struct MtpLayout {
-  size_t acc, acc2, a, hcur, xo, argkey, u, x, total;
+  size_t acc, acc2, gu, a, hcur, xo, argkey, u, x, total;
 };
 
 MtpLayout mtp_layout(const mv_config &c, int Fm, int B) {
@@ -623,7 +623,11 @@ MtpLayout mtp_layout(const mv_config &c, int Fm, int B) {
   };
   L.acc = take(mv::kMtpSplit * b * d * 4);   // K-split partials of z
   L.acc2 = take(mv::kMtpSplit * b * d * 4);  // and of y
-  L.a = take(b * static_cast<size_t>(Fm) * es);
+  // and of the FFN's gate and up (up to kMtpFusedMaxB sequences; above, the
+  // FFN's SwiGLU products a)
+  const bool fused = b <= static_cast<size_t>(mv::kMtpFusedMaxB);
+  L.gu = take(fused ? mv::kMtpSplit * b * 2 * static_cast<size_t>(Fm) * 4 : 0);
+  L.a = take(fused ? 0 : b * static_cast<size_t>(Fm) * es);
   L.hcur = take(b * d * es);
   L.xo = take(b * d * es);
   L.argkey = take(2 * b * 8);
@@ -717,13 +721,14 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
   a.norm_out = m->norm_out;
   a.acc = reinterpret_cast<float *>(base + L.acc);
   a.acc2 = reinterpret_cast<float *>(base + L.acc2);
+  a.gu = reinterpret_cast<float *>(base + L.gu);
   a.xo = base + L.xo;
   a.u = base + L.u;
   a.x = base + L.x;
 
   const mv::ExpertArgs proj = dense_args(*cfg, B, 2 * d, nullptr, m->w_proj, a.acc);
   mv::ExpertArgs gate_up = dense_args(*cfg, B, m->d_ff, nullptr, m->w_gate_up, nullptr);
-  gate_up.a_out = base + L.a;
+  gate_up.a_out = base + L.a;  // above kMtpFusedMaxB sequences
   const mv::ExpertArgs down = dense_args(*cfg, B, m->d_ff, base + L.a, m->w_down, a.acc2);
   for (int step = 0; step < K; ++step) {
     // this position's LM head folds into key buffer step % 2

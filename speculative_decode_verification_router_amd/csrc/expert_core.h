@@ -130,23 +130,44 @@ __device__ __forceinline__ void store_through(bf16_t *p, float v, int lane) {
 // batch; finish() runs the MFMAs with this lane's A row at `arow` (LDS),
 // exchanges the up accumulators and writes a (one block barrier inside).
 // DB: two weight batches in flight (U more registers).
+// ks / ns (begin): this block takes part ks of ns equal parts of the K
+// windows, for partial gate and up outputs (finish_partial) that the reader
+// adds up before the SiLU.
 template <typename T, int U = kUnroll, bool DB = false>
 struct GateUpPart {
   const T *b;
-  int f0, which, slice, nwin;
+  int f0, which, slice, w_lo, w_hi;
   uint4 q[U];
   uint4 q2[DB ? U : 1];  // second weight buffer (DB: two batches in flight)
-  __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid) {
+  __device__ __forceinline__ void begin(const ExpertArgs &p, const TileInfo &ti, int pair, int tid, int ks = 0,
+                                        int ns = 1) {
     constexpr int VN = Vec<T>::N;
     const int lane = tid & 63, wv = tid >> 6;
     slice = wv >> 1;
     which = wv & 1;  // 0 gate rows, 1 up rows
     f0 = (pair * 2 + slice) * 16;
     const int d = p.d, F = p.F, r = lane & 15, koff = (lane >> 4) * VN;
-    nwin = f0 < F ? d / (4 * VN) : 0;
+    const int nwin = d / (4 * VN);
+    w_lo = f0 < F ? ks * nwin / ns : 0;
+    w_hi = f0 < F ? (ks + 1) * nwin / ns : 0;
     const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(2) * F * d);
     b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
-    load_batch<T, U>(q, b, 0, nwin);
+    load_batch<T, U>(q, b, w_lo, w_hi);
+  }
+  // The raw gate (which = 0) or up (which = 1) accumulators of rows [0, m):
+  // out[row * 2F + which * F + f0 + column] for tile row `row` (ti.r0 + row
+  // of the batch), out already offset to this block's K part.
+  __device__ __forceinline__ void finish_partial(const ExpertArgs &p, const TileInfo &ti, const T *arow, float *out,
+                                                 int tid) {
+    const int lane = tid & 63, F = p.F;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    mfma_panel<T, U>(acc, arow, b, w_lo, w_hi, q);
+    if (f0 >= F) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < ti.m) out[static_cast<size_t>(ti.r0 + row) * 2 * F + which * F + f0 + (lane & 15)] = acc[i];
+    }
   }
   // kThrough: a is written with write-through stores (read by other blocks
   // of the same launch).
@@ -155,8 +176,8 @@ struct GateUpPart {
                                          float (*up_acc)[64][4], int tid) {
     const int lane = tid & 63, F = p.F;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (DB) mfma_panel2<T, U>(acc, arow, b, 0, nwin, q, q2);
-    else mfma_panel<T, U>(acc, arow, b, 0, nwin, q);
+    if constexpr (DB) mfma_panel2<T, U>(acc, arow, b, w_lo, w_hi, q, q2);
+    else mfma_panel<T, U>(acc, arow, b, w_lo, w_hi, q);
     if (which == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) up_acc[slice][lane][i] = acc[i];

@@ -11,9 +11,9 @@
 //                 the LM head's argmax key), and block (0, 0) records the
 //                 previous draft and clears the key buffer this position's
 //                 LM head will fold into
-//   k_mtp_ffn_gu  a = R(SiLU(x Wg^T) * (x Wu^T)), x = R(RMSNorm(R(z)) * g_ffn)
-//                 built in LDS by each block
-//   k_mtp_ffn_dn  y = a W_down^T
+//   k_mtp_ffn_gu  g = x Wg^T, u = x Wu^T, x = R(RMSNorm(R(z)) * g_ffn) built
+//                 in LDS by each block
+//   k_mtp_ffn_dn  y = a W_down^T, a = R(SiLU(g) * u) formed while staged
 //   k_mtp_out     h2 = R(R(z) + y) (the next position's h), x_o = R(RMSNorm(h2) * g_out)
 //   (LM head)     the verify step's k_lm_argmax on x_o
 //
@@ -22,10 +22,14 @@
 // argmax keys alternate between two buffers by position parity, so a
 // projection reads the previous position's keys while its block (0, 0)
 // clears the other buffer.  The weight streams are the expert-tile parts of
-// expert_core.h with kUnrollFused windows per batch.  The projection and the
-// FFN down split K into kMtpSplit parts, one block each (their grids are
-// small otherwise), and write fp32 partials that their readers (the FFN's
-// norm, the output kernel) add in part order.
+// expert_core.h with kUnrollFused windows per batch.  The projection, the
+// FFN down and (up to kMtpFusedMaxB sequences) the FFN gate/up split K into
+// kMtpSplit parts, one block each (their grids are small otherwise), and
+// write fp32 partials that their readers add in part order: the FFN's norm
+// (z), the FFN down while it forms a = R(SiLU(g) * u) (g, u), the output
+// kernel (z, y).  Above kMtpFusedMaxB sequences the gate/up writes a itself:
+// there the down blocks of two or more 16-row tiles would each form a whole
+// tile's a from the partials.
 // A row's sum of squares is taken per 16-byte chunk in order, then over the
 // chunks as in the verify step's RMSNorm.
 #include "expert_core.h"
@@ -170,7 +174,6 @@ template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_gu(ExpertArgs p, MtpArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float inv[kTileM];
-  __shared__ float up_acc[2][64][4];
   constexpr int VN = Vec<T>::N;
   const int d = a.d, nvec = d / VN, lda = d + VN, tid = threadIdx.x, lane = tid & 63;
   const int r0 = blockIdx.y * kTileM, m = min(kTileM, a.B - r0);
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_gu(ExpertArgs p, MtpArg
   float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(kTileM) * lda * sizeof(T));
   const TileInfo ti{0, r0, m};
   GateUpPart<T, kDenseU> part_w;
-  part_w.begin(p, ti, blockIdx.x, tid);
+  part_w.begin(p, ti, blockIdx.x, tid, blockIdx.z, kMtpSplit);
   auto h1v = [&](int r, int ch, float *v) {  // h1 = R(z)
     ld_parts<VN>(a.acc + static_cast<size_t>(r0 + r) * d + ch * VN, static_cast<size_t>(a.B) * d, v);
 #pragma unroll
@@ -211,10 +214,15 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_gu(ExpertArgs p, MtpArg
     }
   }
   __syncthreads();
-  part_w.template finish<false>(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, up_acc, tid);
+  part_w.finish_partial(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN,
+                        a.gu + static_cast<size_t>(blockIdx.z) * a.B * 2 * p.F, tid);
 }
 
-template <typename T>
+// A dense projection of a 16-row tile of the rows at p.a (width p.F): the
+// projection or the FFN down above kMtpFusedMaxB sequences; or (kFromGu) the
+// FFN down whose tile a = R(SiLU(g) * u) is formed from the gate/up partials
+// as it is staged.
+template <typename T, bool kFromGu>
 __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_dn(ExpertArgs p, MtpArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int rows[kTileM];
@@ -225,7 +233,27 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_dn(ExpertArgs p, MtpArg
   DownPart<T, kDenseU> part_w;
   part_w.begin(p, ti, blockIdx.x, threadIdx.x, nullptr, nullptr, blockIdx.z, kMtpSplit);
   if (threadIdx.x < kTileM) rows[threadIdx.x] = r0 + threadIdx.x;
-  stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
+  if constexpr (kFromGu) {  // a = R(SiLU(g) * u) of rows [0, m), zero rows past m
+    const int F = p.F, nv = F / VN, ldf = F + VN;
+    const size_t part_stride = static_cast<size_t>(a.B) * 2 * F;
+    T *A = reinterpret_cast<T *>(smem);
+    for (int it = threadIdx.x; it < kTileM * nv; it += blockDim.x) {
+      const int rr = it / nv, c = it - rr * nv;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rr < ti.m) {
+        const float *gp = a.gu + static_cast<size_t>(r0 + rr) * 2 * F + c * VN;
+        float g[VN], u[VN], o[VN];
+        ld_parts<VN>(gp, part_stride, g);
+        ld_parts<VN>(gp + F, part_stride, u);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) o[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+        v = pack(o, T());
+      }
+      st16(A + rr * ldf + c * VN, v);
+    }
+  } else {
+    stage_a_tile<T>(p, ti, reinterpret_cast<T *>(smem), threadIdx.x, blockDim.x);
+  }
   __syncthreads();
   part_w.finish(p, ti, reinterpret_cast<const T *>(smem) + (lane & 15) * (p.F + VN) + (lane >> 4) * VN, half_acc,
                 threadIdx.x, rows, nullptr, static_cast<size_t>(blockIdx.z) * a.B * a.d);
@@ -388,46 +416,54 @@ size_t mtp_ffn_lds(int d, int F, int es) {
 hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertArgs &gu, const ExpertArgs &dn,
                                const MtpArgs &a, int step, hipStream_t s) {
   const int ntiles = (a.B + kTileM - 1) / kTileM, es = dtype == 1 ? 2 : 4;
-  const dim3 g_proj((a.d + 31) / 32, ntiles, kMtpSplit), g_gu((gu.F + 31) / 32, ntiles),
+  const bool fused = a.B <= kMtpFusedMaxB;
+  const dim3 g_proj((a.d + 31) / 32, ntiles, kMtpSplit), g_gu((gu.F + 31) / 32, ntiles, fused ? kMtpSplit : 1),
       g_dn((a.d + 31) / 32, ntiles, kMtpSplit);
   const size_t l_proj = mtp_proj_lds(a.d, es);
   const size_t l_gu = mtp_gu_lds(a.d, es);
   const size_t l_dn = static_cast<size_t>(kTileM) * (dn.F + 16 / es) * es;
   const int last = step == a.K - 1;
-  const bool fused = a.B <= kMtpFusedMaxB;
   ExpertArgs proj_u = proj;  // the row-kernel path's projection reads u from global
   proj_u.a = a.u;
   if (dtype == 1) {
     set_lds(k_mtp_proj<bf16_t>, l_proj);
     set_lds(k_mtp_ffn_gu<bf16_t>, l_gu);
     set_lds(k_mtp_dense_gu<bf16_t>, l_gu);
-    set_lds(k_mtp_ffn_dn<bf16_t>, l_proj > l_dn ? l_proj : l_dn);
+    set_lds(k_mtp_ffn_dn<bf16_t, false>, l_proj > l_dn ? l_proj : l_dn);
+    set_lds(k_mtp_ffn_dn<bf16_t, true>, l_dn);
     if (fused) {
       hipLaunchKernelGGL(k_mtp_proj<bf16_t>, g_proj, dim3(kRowThreads), l_proj, s, proj, a, step);
       hipLaunchKernelGGL(k_mtp_ffn_gu<bf16_t>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
     } else {
       hipLaunchKernelGGL(k_mtp_in<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, step);
-      hipLaunchKernelGGL(k_mtp_ffn_dn<bf16_t>, g_proj, dim3(kRowThreads), l_proj, s, proj_u, a);
+      hipLaunchKernelGGL((k_mtp_ffn_dn<bf16_t, false>), g_proj, dim3(kRowThreads), l_proj, s, proj_u, a);
       hipLaunchKernelGGL(k_mtp_mid<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a);
       hipLaunchKernelGGL(k_mtp_dense_gu<bf16_t>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
     }
-    hipLaunchKernelGGL(k_mtp_ffn_dn<bf16_t>, g_dn, dim3(kRowThreads), l_dn, s, dn, a);
+    if (fused)
+      hipLaunchKernelGGL((k_mtp_ffn_dn<bf16_t, true>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
+    else
+      hipLaunchKernelGGL((k_mtp_ffn_dn<bf16_t, false>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
     hipLaunchKernelGGL(k_mtp_out<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
   } else {
     set_lds(k_mtp_proj<float>, l_proj);
     set_lds(k_mtp_ffn_gu<float>, l_gu);
     set_lds(k_mtp_dense_gu<float>, l_gu);
-    set_lds(k_mtp_ffn_dn<float>, l_proj > l_dn ? l_proj : l_dn);
+    set_lds(k_mtp_ffn_dn<float, false>, l_proj > l_dn ? l_proj : l_dn);
+    set_lds(k_mtp_ffn_dn<float, true>, l_dn);
     if (fused) {
       hipLaunchKernelGGL(k_mtp_proj<float>, g_proj, dim3(kRowThreads), l_proj, s, proj, a, step);
       hipLaunchKernelGGL(k_mtp_ffn_gu<float>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
     } else {
       hipLaunchKernelGGL(k_mtp_in<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, step);
-      hipLaunchKernelGGL(k_mtp_ffn_dn<float>, g_proj, dim3(kRowThreads), l_proj, s, proj_u, a);
+      hipLaunchKernelGGL((k_mtp_ffn_dn<float, false>), g_proj, dim3(kRowThreads), l_proj, s, proj_u, a);
       hipLaunchKernelGGL(k_mtp_mid<float>, dim3(a.B), dim3(kRowThreads), 0, s, a);
       hipLaunchKernelGGL(k_mtp_dense_gu<float>, g_gu, dim3(kRowThreads), l_gu, s, gu, a);
     }
-    hipLaunchKernelGGL(k_mtp_ffn_dn<float>, g_dn, dim3(kRowThreads), l_dn, s, dn, a);
+    if (fused)
+      hipLaunchKernelGGL((k_mtp_ffn_dn<float, true>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
+    else
+      hipLaunchKernelGGL((k_mtp_ffn_dn<float, false>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
     hipLaunchKernelGGL(k_mtp_out<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
   }
   return hipGetLastError();

@@ -136,9 +136,9 @@ struct LmArgs {
 // FastMTP draft block (k_mtp.hip).  Buffers are [B, ...] rows in the
 // config dtype unless noted.
 constexpr int kMtpMaxD = 4096;
-// The projection and the FFN down split K into this many parts, one block
-// each (enough blocks to stream from most of the chip); their readers add
-// the fp32 partial outputs in part order.
+// The projection and the FFN's gate/up and down split K into this many
+// parts, one block each (enough blocks to stream from most of the chip);
+// their readers add the fp32 partial outputs in part order.
 constexpr int kMtpSplit = 2;
 struct MtpArgs {
   int B, K, d, V;
@@ -153,6 +153,7 @@ struct MtpArgs {
   const void *norm_h, *norm_e, *norm_ffn, *norm_out;  // [d]
   float *acc;                    // [kMtpSplit, B, d] fp32 projection output z, partial over K
   float *acc2;                   // [kMtpSplit, B, d] fp32 FFN output y, partial over K
+  float *gu;                     // [kMtpSplit, B, 2F] fp32 FFN gate and up, partial over K
   void *xo;                      // [B, d] LM-head input
   void *u;                       // [B, 2d] projection input (row-kernel path)
   void *x;                       // [B, d] FFN input (row-kernel path)
