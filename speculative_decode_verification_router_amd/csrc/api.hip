@@ -735,7 +735,7 @@ MV_API int mtp_draft(const mv_config *cfg, const mv_weights *w, const mtp_weight
     const mv::LmArgs la{B, d, cfg->vocab, a.xo, w->lm_head, a.argkey + static_cast<size_t>(step & 1) * B, nullptr,
                         mv::AcceptArgs{}};
     if ((rc = hip_status(mv::launch_mtp_position(dt, proj, gate_up, down, a, step, s))) ||
-        (rc = hip_status(mv::launch_lm_argmax(dt, la, s))))
+        (rc = hip_status(mv::launch_mtp_lm(dt, la, a, step, s))))
       return rc;
   }
   return hip_status(mv::launch_mtp_last(a, s));

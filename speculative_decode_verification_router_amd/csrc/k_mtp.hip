@@ -17,6 +17,9 @@
 //   k_mtp_out     h2 = R(R(z) + y) (the next position's h), x_o = R(RMSNorm(h2) * g_out)
 //   (LM head)     the verify step's k_lm_argmax on x_o
 //
+// Up to kMtpFoldMaxB sequences the output kernel's work runs in the LM
+// head's blocks (k_mtp_lm), so a position is four launches.
+//
 // and k_mtp_last reads the last draft.  Above kMtpFusedMaxB sequences the
 // norms run in row kernels instead (k_mtp_in, k_mtp_mid; see below).  The
 // argmax keys alternate between two buffers by position parity, so a
@@ -33,6 +36,7 @@
 // A row's sum of squares is taken per 16-byte chunk in order, then over the
 // chunks as in the verify step's RMSNorm.
 #include "expert_core.h"
+#include "lm_core.h"
 
 namespace mv {
 
@@ -386,6 +390,57 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_out(MtpArgs a, int last) {
   }
 }
 
+// The LM head of a draft position up to kMtpFoldMaxB sequences with the
+// output kernel folded in: each block requests its first weights, then forms
+// the rows' x_o = R(RMSNorm(h2) * g_out), h2 = R(R(z) + y) from the
+// projection's and the FFN's partials (the arithmetic of k_mtp_out, row for
+// row), and block 0 also writes h2, the next position's input (and, after
+// the last position, h_out).  The keys fold into p.argkey.
+template <typename T>
+__global__ __launch_bounds__(64 * kLmWaves) void k_mtp_lm(LmArgs p, MtpArgs a, int last) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ unsigned long long red[kLmWaves][kTileM];
+  __shared__ float inv[kMtpFoldMaxB];
+  constexpr int VN = Vec<T>::N;
+  const int m = a.B, d = a.d, nvec = d / VN, lda = d + VN, tid = threadIdx.x, lane = tid & 63;
+  T *A = reinterpret_cast<T *>(smem);  // rows [0, m) of x_o, then a zero row
+  float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(m + 1) * lda * sizeof(T));
+  LmStream<T> ls;
+  ls.begin(p, blockIdx.x, tid);  // weights requested before x_o is formed
+  const size_t stride = static_cast<size_t>(a.B) * d;
+  auto hv = [&](int r, int ch, float *v) {  // h2 = R(R(z) + y)
+    float q[VN];
+    ld_parts<VN>(a.acc + static_cast<size_t>(r) * d + ch * VN, stride, v);
+    ld_parts<VN>(a.acc2 + static_cast<size_t>(r) * d + ch * VN, stride, q);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) v[i] = round_to<T>(round_to<T>(v[i]) + q[i]);
+  };
+  tile_inv_rms<VN>(m, d, a.eps, part, inv, hv);
+  const T *go = static_cast<const T *>(a.norm_out);
+  T *hc = static_cast<T *>(a.h_cur), *ho = last && a.h_out ? static_cast<T *>(a.h_out) : nullptr;
+  for (int it = tid; it < (m + 1) * nvec; it += blockDim.x) {
+    const int r = it / nvec, ch = it - r * nvec;
+    uint4 xo = make_uint4(0, 0, 0, 0);
+    if (r < m) {
+      float v[VN], g[VN], o[VN];
+      hv(r, ch, v);
+      if (blockIdx.x == 0) {
+        const uint4 pk = pack(v, T());
+        st16(hc + static_cast<size_t>(r) * d + ch * VN, pk);
+        if (ho) st16(ho + static_cast<size_t>(r) * d + ch * VN, pk);
+      }
+      unpack(ld16(go + ch * VN), g, T());
+#pragma unroll
+      for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[i] * inv[r]) * g[i]);
+      xo = pack(o, T());
+    }
+    st16(A + r * lda + ch * VN, xo);
+  }
+  __syncthreads();
+  const int arow = (lane & 15) < m ? (lane & 15) : m;
+  ls.finish(p, 0, m, A + arow * lda + (lane >> 4) * VN, red, tid);
+}
+
 __global__ void k_mtp_last(MtpArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   const unsigned long long *key = a.argkey + static_cast<size_t>((a.K - 1) & 1) * a.B;
@@ -444,7 +499,8 @@ hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertAr
       hipLaunchKernelGGL((k_mtp_ffn_dn<bf16_t, true>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
     else
       hipLaunchKernelGGL((k_mtp_ffn_dn<bf16_t, false>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
-    hipLaunchKernelGGL(k_mtp_out<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
+    if (a.B > kMtpFoldMaxB)  // otherwise the LM head forms h2 and x_o (k_mtp_lm)
+      hipLaunchKernelGGL(k_mtp_out<bf16_t>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
   } else {
     set_lds(k_mtp_proj<float>, l_proj);
     set_lds(k_mtp_ffn_gu<float>, l_gu);
@@ -464,7 +520,25 @@ hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertAr
       hipLaunchKernelGGL((k_mtp_ffn_dn<float, true>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
     else
       hipLaunchKernelGGL((k_mtp_ffn_dn<float, false>), g_dn, dim3(kRowThreads), l_dn, s, dn, a);
-    hipLaunchKernelGGL(k_mtp_out<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
+    if (a.B > kMtpFoldMaxB)  // otherwise the LM head forms h2 and x_o (k_mtp_lm)
+      hipLaunchKernelGGL(k_mtp_out<float>, dim3(a.B), dim3(kRowThreads), 0, s, a, last);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mtp_lm(int dtype, const LmArgs &la, const MtpArgs &a, int step, hipStream_t s) {
+  if (a.B > kMtpFoldMaxB) return launch_lm_argmax(dtype, la, s);
+  if (la.T != a.B || la.d != a.d || la.done) return hipErrorInvalidValue;
+  const int es = dtype == 1 ? 2 : 4, last = step == a.K - 1;
+  const dim3 grid((la.V + kLmRowsPerBlock - 1) / kLmRowsPerBlock);
+  const size_t smem = static_cast<size_t>(a.B + 1) * (a.d + 16 / es) * es +
+                      static_cast<size_t>(a.B) * (a.d / (16 / es)) * 4;
+  if (dtype == 1) {
+    set_lds(k_mtp_lm<bf16_t>, smem);
+    hipLaunchKernelGGL(k_mtp_lm<bf16_t>, grid, dim3(64 * kLmWaves), smem, s, la, a, last);
+  } else {
+    set_lds(k_mtp_lm<float>, smem);
+    hipLaunchKernelGGL(k_mtp_lm<float>, grid, dim3(64 * kLmWaves), smem, s, la, a, last);
   }
   return hipGetLastError();
 }

@@ -161,15 +161,22 @@ struct MtpArgs {
 // Up to this many sequences the projection and gate/up kernels normalise
 // their tiles themselves (at most one row per wavefront).
 constexpr int kMtpFusedMaxB = 4;
+// Up to this many sequences the LM head's blocks form the position's output
+// rows themselves (at 4 each block's extra rows cost more than the launch).
+constexpr int kMtpFoldMaxB = 3;
 // Dynamic LDS of the projection and FFN kernels, bytes (es: element size).
 size_t mtp_proj_lds(int d, int es);
 size_t mtp_ffn_lds(int d, int F, int es);
-// The four launches of one draft position before its LM head; proj, gu and
+// The launches of one draft position before its LM head; proj, gu and
 // dn are one-expert arguments (E = 1, k = 0, nslot = 1) of the projection
 // (F = 2d, slots = acc), the FFN gate/up (a_out) and the FFN down (slots = acc2).
 hipError_t launch_mtp_position(int dtype, const ExpertArgs &proj, const ExpertArgs &gu, const ExpertArgs &dn,
                                const MtpArgs &a, int step, hipStream_t s);
 hipError_t launch_mtp_last(const MtpArgs &a, hipStream_t s);
+// The LM head of draft position `step` (la: keys of this position, no block
+// counter); up to kMtpFoldMaxB sequences it also forms h2 and x_o, which
+// launch_mtp_position then leaves to it.
+hipError_t launch_mtp_lm(int dtype, const LmArgs &la, const MtpArgs &a, int step, hipStream_t s);
 
 // One-launch verify step for batches routed to logits (k_expert.hip): the
 // step's launches become virtual blocks of one launch of resident blocks.

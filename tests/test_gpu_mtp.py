@@ -83,7 +83,7 @@ def _compare(bd, torch, dims, W, M, model, mtp, h, tokens, K, alias=False):
     return got, ref
 
 
-@pytest.mark.parametrize("B,K", [(1, 1), (4, 3), (17, 3), (5, 15)])
+@pytest.mark.parametrize("B,K", [(1, 1), (3, 3), (4, 3), (17, 3), (5, 15)])
 def test_mtp_tiny_fp32(bd, torch_cuda, tiny, B, K):
     dims, W, M, model, mtp = tiny
     h = synth.make_hidden(dims, B, code=30 + B)
@@ -108,7 +108,7 @@ def test_mtp_h_out_may_alias_h_in(bd, torch_cuda, tiny):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("B", [1, 4, 16])
+@pytest.mark.parametrize("B", [1, 3, 4, 16])
 def test_mtp_bf16_full_width(bd, torch_cuda, big, B):
     dims, W, M, model, mtp = big
     h = synth.make_hidden(dims, B, code=50 + B)
