@@ -148,14 +148,12 @@ int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B,
  * rows (B*(K+1) <= 8) and at most 16 layers; arguments, results and
  * workspace as in moe_verify_step, and the results are bit-identical to it.
  * A small setup kernel writes the step's arguments into the workspace and
- * clears its counters; one cooperative launch of resident blocks then runs
- * every layer's routing and experts, the final norm and the LM head with the
- * accept rule, each block working through the step's virtual blocks in
- * order, so that the next layer's shared experts and the LM head can stream
- * their weights while the previous stage finishes.  Errors: larger batches
- * or more layers MV_ERR_UNSUPPORTED; MV_ERR_HIP if the kernel cannot be made
- * resident on the device.  A wait that gives up sets the status word
- * (mv_step_status), as in moe_verify_step. */
+ * clears its counters; one launch then runs every layer's routing and
+ * experts, the final norm and the LM head with the accept rule, its blocks
+ * in step order, so that the next layer's shared experts and the LM head can
+ * stream their weights while the previous stage finishes.  Errors: larger
+ * batches or more layers MV_ERR_UNSUPPORTED.  A wait that gives up sets the
+ * status word (mv_step_status), as in moe_verify_step. */
 int moe_verify_step_one_launch(const mv_config *cfg, const mv_weights *w, int32_t B,
                                int32_t K, const void *h_in, const int32_t *drafts,
                                void *h_out, int32_t *argmax, int32_t *n_accepted,

@@ -496,7 +496,7 @@ int scratch_on_device(void **out) {
 // The verify step of a batch routed to logits as one launch: the setup kernel
 // writes every virtual block's arguments and clears the counters, then
 // k_one_launch runs the layers' fused launches, the final norm and the LM
-// head with the accept rule as virtual blocks of resident blocks.  Buffers
+// head with the accept rule as the blocks of one launch.  Buffers
 // and arithmetic are those of verify_launches, so the results are
 // bit-identical to moe_verify_step's.
 int one_launch_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K, const void *h_in,
@@ -545,10 +545,8 @@ int one_launch_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_
   a.h_last = cur;
   a.h_final = hbuf;
   const size_t smem = mv::one_launch_smem(cfg->dtype, T, cfg->d_model, cfg->d_ff);
-  const int blocks = mv::one_launch_blocks(cfg->dtype, smem);
-  if (blocks <= 0) return fail(MV_ERR_HIP, "the one-launch verify step cannot be made resident on this device");
   return hip_status(mv::launch_one_launch(cfg->dtype, a, reinterpret_cast<mv::OneLaunchDev *>(st.ws + st.L.ol_args),
-                                          st.status(), blocks, smem, st.s));
+                                          st.status(), smem, st.s));
 }
 
 MV_API int moe_verify_step(const mv_config *cfg, const mv_weights *w, int32_t B, int32_t K,

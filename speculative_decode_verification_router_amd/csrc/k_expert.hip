@@ -395,26 +395,19 @@ __global__ __launch_bounds__(kThreads) void k_ffn_small(ExpertArgs p, RouteArgs 
 
 // ------------------------------------------------- one-launch verify step
 //
-// The verify step of a batch routed to logits as one launch of resident
-// blocks.  Its launches become virtual blocks, numbered in launch order: per
-// layer the fused launch's blocks (routing, gate/up, down; layer 0 routes
-// inside it too), then one final-norm block per token, then the LM head's
-// blocks, whose last one applies the accept rule.  A resident block that is
-// free takes the next virtual block number from a counter, so the numbers
-// are handed out in increasing order, and runs it with the code of the
-// launch it stands for.  Every wait is for virtual blocks of lower number: a
-// layer's routing for every expert block of the previous layer (which also
-// keeps each buffer the layers share from being overwritten while it is
-// read), its expert blocks as in the fused launch, the final norm for the
-// last layer, the LM head for the final norm.  So the lowest unfinished
-// virtual block that has been taken has all its inputs, and its block is
-// running it (every block runs its virtual blocks in increasing order, and
-// one that is free takes a new one): with all
-// blocks resident (a cooperative launch) the launch cannot deadlock, and the
-// waits are bounded as in the fused launch.  Data another block of the launch
-// reads is written through and read with agent-scope loads.  Per virtual
-// block the arithmetic is that of the block it stands for (route_fused is
-// route_block's in both modes), so results are bit-identical to the launches.
+// The verify step of a batch routed to logits as one launch.  Its launches
+// become virtual blocks, numbered in launch order: per layer the fused
+// launch's blocks (routing, gate/up, down; layer 0 routes inside it too),
+// then one final-norm block per token, then the LM head's blocks, whose last
+// one applies the accept rule.  Every wait is for virtual blocks of lower
+// number: a layer's routing for every expert block of the previous layer
+// (which also keeps each buffer the layers share from being overwritten while
+// it is read), its expert blocks as in the fused launch, the final norm for
+// the last layer, the LM head for the final norm.  Data another block of the
+// launch reads is written through and read with agent-scope loads.  Per
+// virtual block the arithmetic is that of the block it stands for
+// (route_fused is route_block's in both modes), so results are bit-identical
+// to the launches.
 // One block: every layer's arguments from the shared ones and the layer's
 // pointers; all blocks: the counters and the status word cleared.
 __global__ __launch_bounds__(256) void k_one_launch_setup(OneLaunchArgs a, OneLaunchDev *dev, unsigned *status) {
@@ -488,33 +481,24 @@ __device__ __forceinline__ void one_launch_lm_block(const LmArgs &p, int vblk, i
   lm_block_done(p, static_cast<unsigned>(n_lm));
 }
 
+// The step kernel: one hardware block per virtual block, in virtual-block
+// order.  The hardware hands a launch's blocks out in increasing order and
+// every wait is for lower-numbered blocks, so the lowest unfinished block has
+// been dispatched and has every input (the fused launch's argument): the
+// launch cannot deadlock, and its waits are bounded as in the fused launch.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_one_launch(const OneLaunchDev *__restrict__ dev, int L, int T_,
-                                                            int n_route, int n_expert, int max_tiles, int n_lm,
-                                                            int set_lines, unsigned *ctr, unsigned *err,
-                                                            int spin_limit) {
+__global__ __launch_bounds__(kThreads) void k_one_launch(const OneLaunchDev *__restrict__ dev, int L, int T_,
+                                                       int n_route, int n_expert, int max_tiles, int n_lm,
+                                                       int set_lines, unsigned *ctr, unsigned *err, int spin_limit) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ SmallTiles st;
   __shared__ float xacc[2][64][4];
   __shared__ unsigned long long red[kLmWaves][kTileM];
   const int per_layer = n_route + n_expert;
-  const int n_layers_vb = L * per_layer, total = n_layers_vb + T_ + n_lm;
+  const int n_layers_vb = L * per_layer;
   unsigned *final_ctr = ctr + static_cast<size_t>(L) * set_lines * kDoneStride;
-  // Each block takes the next virtual block number from a counter when it is
-  // free (in increasing order, as the hardware hands out a launch's blocks);
-  // one loop per kind, in order (each loop's registers are its own): the
-  // layers', the final norms', the LM head's.
-  __shared__ int vb_s;
-  unsigned *vb_ctr = final_ctr + 2 * kDoneStride;
-  auto take = [&]() {
-    __syncthreads();  // the previous virtual block's LDS and vb_s
-    if (threadIdx.x == 0)
-      vb_s = static_cast<int>(__hip_atomic_fetch_add(vb_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    __syncthreads();
-    return vb_s;
-  };
-  int vb = take();
-  for (; vb < n_layers_vb; vb = take()) {
+  const int vb = static_cast<int>(blockIdx.x);
+  if (vb < n_layers_vb) {
     const int l = vb / per_layer, local = vb - l * per_layer;
     unsigned *done_l = ctr + (static_cast<size_t>(l) * set_lines + max_tiles + kRouteCopies) * kDoneStride;
     if (local < n_route && l > 0) {  // the previous layer's expert blocks have finished
@@ -528,15 +512,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_one_launch(const OneLaunchDev *
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_fetch_add(done_l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    return;
   }
-  for (; vb < n_layers_vb + T_; vb = take()) {  // final combine and norm of one token
+  if (vb < n_layers_vb + T_) {  // final combine and norm of one token
     wait_count(final_ctr - static_cast<size_t>(set_lines - max_tiles - kRouteCopies) * kDoneStride,
                static_cast<unsigned>(n_expert), err, spin_limit);
     __syncthreads();
     one_launch_final_block<T>(dev, vb - n_layers_vb, smem, final_ctr);
+    return;
   }
-  for (; vb < total; vb = take())  // LM-head blocks over all T rows (T <= 16)
-    one_launch_lm_block<T>(dev->lm, vb - n_layers_vb - T_, n_lm, final_ctr, err, spin_limit, smem, red);
+  one_launch_lm_block<T>(dev->lm, vb - n_layers_vb - T_, n_lm, final_ctr, err, spin_limit, smem, red);
 }
 
 // ------------------------------------------------------------ medium batches
@@ -749,31 +734,23 @@ size_t one_launch_smem(int dtype, int T, int d, int F) {
   return smem > route ? smem : route;
 }
 
-int one_launch_blocks(int dtype, size_t smem) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))
-    return 0;
-  const void *f = dtype == 1 ? reinterpret_cast<const void *>(k_one_launch<bf16_t>)
-                             : reinterpret_cast<const void *>(k_one_launch<float>);
-  if (smem > 48 * 1024) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kThreads, smem) != hipSuccess) return 0;
-  return per_cu * cus;
-}
-
-hipError_t launch_one_launch(int dtype, const OneLaunchArgs &a, OneLaunchDev *dev, unsigned *status, int blocks,
-                             size_t smem, hipStream_t s) {
+hipError_t launch_one_launch(int dtype, const OneLaunchArgs &a, OneLaunchDev *dev, unsigned *status, size_t smem,
+                             hipStream_t s) {
   hipLaunchKernelGGL(k_one_launch_setup, dim3(16), dim3(256), 0, s, a, dev, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const OneLaunchDev *cdev = dev;
-  int L = a.L, T = a.e.T, n_route = a.n_route, mt = a.max_tiles, n_lm = a.n_lm, sl = a.set_lines;
-  int n_expert = ((a.e.F + 31) / 32 + (a.e.d + 31) / 32) * mt;
-  unsigned *ctr = a.ctr, *err = a.e.err;
-  int spin = a.e.spin_limit;
-  void *args[] = {&cdev, &L, &T, &n_route, &n_expert, &mt, &n_lm, &sl, &ctr, &err, &spin};
-  const void *f = dtype == 1 ? reinterpret_cast<const void *>(k_one_launch<bf16_t>)
-                             : reinterpret_cast<const void *>(k_one_launch<float>);
-  return hipLaunchCooperativeKernel(f, dim3(blocks), dim3(kThreads), args, static_cast<unsigned>(smem), s);
+  const int n_expert = ((a.e.F + 31) / 32 + (a.e.d + 31) / 32) * a.max_tiles;
+  const int T = a.e.T, total = a.L * (a.n_route + n_expert) + T + a.n_lm;
+  if (dtype == 1) {
+    allow_lds(k_one_launch<bf16_t>, smem);
+    hipLaunchKernelGGL(k_one_launch<bf16_t>, dim3(total), dim3(kThreads), smem, s, dev, a.L, T, a.n_route, n_expert,
+                       a.max_tiles, a.n_lm, a.set_lines, a.ctr, a.e.err, a.e.spin_limit);
+  } else {
+    allow_lds(k_one_launch<float>, smem);
+    hipLaunchKernelGGL(k_one_launch<float>, dim3(total), dim3(kThreads), smem, s, dev, a.L, T, a.n_route, n_expert,
+                       a.max_tiles, a.n_lm, a.set_lines, a.ctr, a.e.err, a.e.spin_limit);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace mv

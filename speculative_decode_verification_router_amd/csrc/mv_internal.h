@@ -179,7 +179,7 @@ hipError_t launch_mtp_last(const MtpArgs &a, hipStream_t s);
 hipError_t launch_mtp_lm(int dtype, const LmArgs &la, const MtpArgs &a, int step, hipStream_t s);
 
 // One-launch verify step for batches routed to logits (k_expert.hip): the
-// step's launches become virtual blocks of one launch of resident blocks.
+// step's launches become the blocks of one launch.
 // Per-layer pointers, and the arguments every layer shares (the per-layer
 // fields of e and r are replaced from `layer`).
 constexpr int kOneLaunchMaxLayers = 16;
@@ -198,13 +198,13 @@ struct OneLaunchArgs {
   const float *slots;
   const void *h_last;  // residual input of the final combine
   void *h_final;       // its output (h_out)
-  unsigned *ctr;       // counter lines: per layer [tiles | routing copies | experts done], then the final norm's, the LM head's and the virtual-block counter
+  unsigned *ctr;       // counter lines: per layer [tiles | routing copies | experts done], then the final norm's and the LM head's
   int L, max_tiles, n_route, n_lm, set_lines;
   StepLayer layer[kOneLaunchMaxLayers];
 };
 // Counter words the one-launch step uses for L layers at max_tiles tiles.
 __host__ __device__ inline size_t one_launch_counter_words(int L, int max_tiles) {
-  return (static_cast<size_t>(L) * (max_tiles + kRouteCopies + 1) + 3) * kDoneStride;
+  return (static_cast<size_t>(L) * (max_tiles + kRouteCopies + 1) + 2) * kDoneStride;
 }
 // The arguments of every virtual block, written into the workspace by the
 // setup kernel and read in place by the step kernel.
@@ -220,11 +220,9 @@ struct OneLaunchDev {
   LmArgs lm;
 };
 size_t one_launch_smem(int dtype, int T, int d, int F);
-// Resident blocks of the one-launch kernel (0 if it cannot run).
-int one_launch_blocks(int dtype, size_t smem);
 // Setup (arguments into dev, counters and status word cleared), then the step.
-hipError_t launch_one_launch(int dtype, const OneLaunchArgs &a, OneLaunchDev *dev, unsigned *status, int blocks,
-                             size_t smem, hipStream_t s);
+hipError_t launch_one_launch(int dtype, const OneLaunchArgs &a, OneLaunchDev *dev, unsigned *status, size_t smem,
+                             hipStream_t s);
 
 // dtype-dispatched launchers (dtype: 0 fp32, 1 bf16); return the launch error.
 hipError_t launch_route(int dtype, const RouteArgs &a, const CombineArgs &c, int ntok, hipStream_t s);
