@@ -656,7 +656,8 @@ def _one_launch_case(bd, torch, dims, model, B, K, seed):
 
 
 @pytest.mark.parametrize("model_name,B,K", [("big", 1, 0), ("big", 1, 3), ("big", 2, 1), ("big", 2, 3),
-                                            ("tiny", 1, 3), ("tiny", 2, 3), ("tiny3", 1, 1), ("tiny3", 2, 3)])
+                                            ("big", 8, 0), ("big", 4, 1), ("tiny", 1, 3), ("tiny", 2, 3),
+                                            ("tiny", 4, 1), ("tiny3", 1, 1), ("tiny3", 2, 3)])
 def test_one_launch_step_equals_the_launches(bd, torch_cuda, tiny, tiny3, big, model_name, B, K):
     """moe_verify_step_one_launch runs the launches' blocks as virtual blocks
     of one launch with the same arithmetic: every output equals
