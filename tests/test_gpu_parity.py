@@ -75,18 +75,22 @@ def tiny3(bd):
 
 
 # Other model shapes the library takes: fewer routed experts (the routing's
-# expert groups, the top-k lanes and the tile search past E), one or three
-# shared experts, top-k of 4, 5 and 8, several layers.  odd16g fits the
-# large-batch GEMM path (d % 256 == 0, d_ff % 128 == 0, at most 2 shared).
+# expert groups, the top-k lanes and the tile search past E), no shared
+# expert and one to four of them, top-k from 1 (a gate of exactly 1) to 8,
+# several layers.  odd16g fits the large-batch GEMM path (d % 256 == 0,
+# d_ff % 128 == 0, at most 2 shared).
 ODD_F32 = synth.ModelDims(128, 64, 20, 1, 4, 3, 300, 1e-6, "f32")
 ODD_BF16 = synth.ModelDims(256, 192, 40, 3, 8, 2, 5000, 1e-6, "bf16")
 ODD_BF16_GEMM = synth.ModelDims(256, 256, 24, 2, 5, 2, 3000, 1e-6, "bf16")
+ODD_NO_SHARED = synth.ModelDims(128, 128, 16, 0, 1, 2, 400, 1e-6, "f32")
+ODD_FOUR_SHARED = synth.ModelDims(256, 128, 32, 4, 2, 2, 2000, 1e-6, "bf16")
 
 
 @pytest.fixture(scope="module")
 def odd(bd):
     out = {}
-    for name, dims, sigma in (("odd32", ODD_F32, None), ("odd16", ODD_BF16, 0.05), ("odd16g", ODD_BF16_GEMM, 0.05)):
+    for name, dims, sigma in (("odd32", ODD_F32, None), ("odd16", ODD_BF16, 0.05), ("odd16g", ODD_BF16_GEMM, 0.05),
+                              ("s0k1", ODD_NO_SHARED, None), ("s4k2", ODD_FOUR_SHARED, 0.05)):
         W = synth.make_weights(dims, seed=11, sigma=sigma, gamma="uniform")
         out[name] = (dims, W, _model(bd, dims, W, 700))
     return out
@@ -444,7 +448,8 @@ def test_router_bias_zipf(bd, torch_cuda, big):
 
 
 @pytest.mark.parametrize("name,T", [("odd32", 4), ("odd32", 100), ("odd32", 300), ("odd16", 4), ("odd16", 100),
-                                    ("odd16", 300), ("odd16g", 600)])
+                                    ("odd16", 300), ("odd16g", 600), ("s0k1", 4), ("s0k1", 100), ("s0k1", 600),
+                                    ("s4k2", 4), ("s4k2", 100), ("s4k2", 600)])
 def test_layer_forward_other_shapes(bd, torch_cuda, odd, name, T):
     """One layer of each odd shape on the 16-row, 64-row and (odd16g, 600
     rows) GEMM paths against the oracle."""
@@ -454,7 +459,8 @@ def test_layer_forward_other_shapes(bd, torch_cuda, odd, name, T):
 
 
 @pytest.mark.parametrize("name,B", [("odd32", 1), ("odd32", 2), ("odd32", 8), ("odd32", 40), ("odd16", 1),
-                                    ("odd16", 2), ("odd16", 8), ("odd16", 40)])
+                                    ("odd16", 2), ("odd16", 8), ("odd16", 40), ("s0k1", 1), ("s0k1", 2),
+                                    ("s0k1", 8), ("s0k1", 40), ("s4k2", 1), ("s4k2", 2), ("s4k2", 8), ("s4k2", 40)])
 def test_verify_other_shapes(bd, torch_cuda, odd, name, B):
     """Verify steps of the odd shapes (B = 1, 2: routing inside the fused
     launch; 8: 16-row tiles; 40: 64-row tiles) against the oracle."""
@@ -464,7 +470,7 @@ def test_verify_other_shapes(bd, torch_cuda, odd, name, B):
     _verify_check(bd, torch_cuda, dims, W, model, h, B, K, 0.6, 7, f"{name} verify B={B}")
 
 
-@pytest.mark.parametrize("name", ["odd32", "odd16"])
+@pytest.mark.parametrize("name", ["odd32", "odd16", "s0k1", "s4k2"])
 def test_other_shapes_same_results_on_every_batch_path(bd, torch_cuda, odd, name):
     """The batch-path invariance on the odd shapes, and the one-launch step
     bit-identical to the launches at B = 1, 2."""
