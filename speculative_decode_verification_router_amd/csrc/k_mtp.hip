@@ -47,6 +47,9 @@ constexpr int kDenseU = kUnrollFused;
 
 // Chunks each thread loads before it uses any of them.
 constexpr int kChunksInFlight = 8;
+// Up to this many chunks per thread a tile's rows are read once, kept in
+// registers between their norm and its use.
+constexpr int kOnePassChunks = 8;
 
 // 1/rms of rows [0, m) of a tile, rows given by val(row, chunk, out[VN]),
 // into inv[row]; part: LDS of m * d / VN floats.  Synchronises the block.
@@ -71,6 +74,32 @@ __device__ __forceinline__ void tile_inv_rms(int m, int d, float eps, float *par
   }
   __syncthreads();
   for (int r = w; r < m; r += blockDim.x / kWave) {
+    float acc = 0.f;
+    for (int ch = lane; ch < nvec; ch += kWave) acc += part[r * nvec + ch];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) inv[r] = 1.0f / sqrtf(acc / static_cast<float>(d) + eps);
+  }
+  __syncthreads();
+}
+
+// tile_inv_rms's sums and reduction for rows [0, m) whose chunks a thread
+// holds in registers: chunk it = threadIdx.x + u * kRowThreads in v[u]
+// (it < n = m * nvec).  Synchronises the block.
+template <int VN>
+__device__ __forceinline__ void one_pass_inv(int m, int nvec, int d, float eps, float *part, float *inv,
+                                             const float (*v)[VN], int n) {
+  const int tid = threadIdx.x, lane = tid & 63;
+#pragma unroll
+  for (int u = 0; u < kOnePassChunks; ++u) {
+    const int it = tid + u * kRowThreads;
+    float s = v[u][0] * v[u][0];
+#pragma unroll
+    for (int i = 1; i < VN; ++i) s = __builtin_fmaf(v[u][i], v[u][i], s);
+    if (it < n) part[it] = s;
+  }
+  __syncthreads();
+  for (int r = tid >> 6; r < m; r += kRowThreads / kWave) {
     float acc = 0.f;
     for (int ch = lane; ch < nvec; ch += kWave) acc += part[r * nvec + ch];
 #pragma unroll
@@ -139,12 +168,61 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_proj(ExpertArgs p, MtpArgs 
   const T *emb = static_cast<const T *>(a.embed);
   auto hv = [&](int r, int ch, float *v) { unpack(ld16(h + static_cast<size_t>(r0 + r) * d + ch * VN), v, T()); };
   auto ev = [&](int r, int ch, float *v) { unpack(ld16(emb + static_cast<size_t>(tok[r]) * d + ch * VN), v, T()); };
+  const T *gh = static_cast<const T *>(a.norm_h), *ge = static_cast<const T *>(a.norm_e);
+  const int nu = m * 2 * nvec;
+  if (nu <= kOnePassChunks * kRowThreads) {
+    // One pass: the 2m rows [h rows | E rows] (row q: h row q, or E row q - m)
+    // and their gamma chunks are loaded once; the chunk sums, the per-row
+    // reduction and u are tile_inv_rms's and the loop below's arithmetic.
+    float v[kOnePassChunks][VN];
+    uint4 gq[kOnePassChunks];
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads, q = it / nvec, ch = it - q * nvec;
+      if (it < nu) {
+        if (q >= m) ev(q - m, ch, v[u]); else hv(q, ch, v[u]);
+        gq[u] = ld16((q >= m ? ge : gh) + ch * VN);
+      }
+    }
+    float *inv_all = inv[0];  // inv[0][r] and inv[1][r] follow each other: row q at inv_all[q < m ? q : kTileM + q - m]
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads;
+      float sq = v[u][0] * v[u][0];
+#pragma unroll
+      for (int i = 1; i < VN; ++i) sq = __builtin_fmaf(v[u][i], v[u][i], sq);
+      if (it < nu) part[it] = sq;
+    }
+    __syncthreads();
+    for (int q = tid >> 6; q < 2 * m; q += kRowThreads / kWave) {
+      float acc = 0.f;
+      for (int ch = lane; ch < nvec; ch += kWave) acc += part[q * nvec + ch];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+      if (lane == 0) inv_all[q < m ? q : kTileM + q - m] = 1.0f / sqrtf(acc / static_cast<float>(d) + a.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads, q = it / nvec, ch = it - q * nvec;
+      if (it >= nu) break;
+      const int half = q >= m, r = q - half * m;
+      float g[VN], o[VN];
+      unpack(gq[u], g, T());
+      const float sc = inv[half][r];
+#pragma unroll
+      for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[u][i] * sc) * g[i]);
+      st16(A + r * lda + (half * nvec + ch) * VN, pack(o, T()));
+    }
+    __syncthreads();
+    part_w.finish(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN, half_acc, tid, rows, nullptr,
+                  static_cast<size_t>(blockIdx.z) * a.B * d);
+    return;
+  }
   tile_inv_rms<VN>(m, d, a.eps, part, inv[0], hv);
   tile_inv_rms<VN>(m, d, a.eps, part, inv[1], ev);
   // u = [R(RMSNorm(h) * g_h) ; R(RMSNorm(E[t]) * g_e)] for rows [0, m) only: an
   // MFMA output row depends on its own A row alone
-  const T *gh = static_cast<const T *>(a.norm_h), *ge = static_cast<const T *>(a.norm_e);
-  const int nu = m * 2 * nvec;
   for (int it0 = tid; it0 < nu; it0 += kChunksInFlight * blockDim.x) {
     float v[kChunksInFlight][VN];
     uint4 gq[kChunksInFlight];
@@ -191,10 +269,37 @@ __global__ __launch_bounds__(kRowThreads) void k_mtp_ffn_gu(ExpertArgs p, MtpArg
 #pragma unroll
     for (int i = 0; i < VN; ++i) v[i] = round_to<T>(v[i]);
   };
-  tile_inv_rms<VN>(m, d, a.eps, part, inv, h1v);
-  // x = R(RMSNorm(h1) * g_ffn) for rows [0, m) (as in k_mtp_proj)
   const T *gf = static_cast<const T *>(a.norm_ffn);
   const int nx = m * nvec;
+  if (nx <= kOnePassChunks * kRowThreads) {  // one pass, as in k_mtp_proj
+    float v[kOnePassChunks][VN];
+    uint4 gq[kOnePassChunks];
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads, r = it / nvec, ch = it - r * nvec;
+      if (it < nx) {
+        h1v(r, ch, v[u]);
+        gq[u] = ld16(gf + ch * VN);
+      }
+    }
+    one_pass_inv<VN>(m, nvec, d, a.eps, part, inv, v, nx);
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads, r = it / nvec;
+      if (it >= nx) break;
+      float g[VN], o[VN];
+      unpack(gq[u], g, T());
+#pragma unroll
+      for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[u][i] * inv[r]) * g[i]);
+      st16(A + r * lda + (it - r * nvec) * VN, pack(o, T()));
+    }
+    __syncthreads();
+    part_w.finish_partial(p, ti, A + (lane & 15) * lda + (lane >> 4) * VN,
+                          a.gu + static_cast<size_t>(blockIdx.z) * a.B * 2 * p.F, tid);
+    return;
+  }
+  tile_inv_rms<VN>(m, d, a.eps, part, inv, h1v);
+  // x = R(RMSNorm(h1) * g_ffn) for rows [0, m) (as in k_mtp_proj)
   for (int it0 = tid; it0 < nx; it0 += kChunksInFlight * blockDim.x) {
     float v[kChunksInFlight][VN];
     uint4 gq[kChunksInFlight];
@@ -415,9 +520,44 @@ __global__ __launch_bounds__(64 * kLmWaves) void k_mtp_lm(LmArgs p, MtpArgs a, i
 #pragma unroll
     for (int i = 0; i < VN; ++i) v[i] = round_to<T>(round_to<T>(v[i]) + q[i]);
   };
-  tile_inv_rms<VN>(m, d, a.eps, part, inv, hv);
   const T *go = static_cast<const T *>(a.norm_out);
   T *hc = static_cast<T *>(a.h_cur), *ho = last && a.h_out ? static_cast<T *>(a.h_out) : nullptr;
+  static_assert(64 * kLmWaves == kRowThreads, "the LM head's blocks have kRowThreads threads");
+  if (m * nvec <= kOnePassChunks * kRowThreads) {  // one pass, as in k_mtp_proj
+    const int n = m * nvec;
+    float v[kOnePassChunks][VN];
+    uint4 gq[kOnePassChunks];
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads, r = it / nvec, ch = it - r * nvec;
+      if (it < n) {
+        hv(r, ch, v[u]);
+        gq[u] = ld16(go + ch * VN);
+      }
+    }
+    one_pass_inv<VN>(m, nvec, d, a.eps, part, inv, v, n);
+#pragma unroll
+    for (int u = 0; u < kOnePassChunks; ++u) {
+      const int it = tid + u * kRowThreads, r = it / nvec, ch = it - r * nvec;
+      if (it >= n) break;
+      if (blockIdx.x == 0) {
+        const uint4 pk = pack(v[u], T());
+        st16(hc + static_cast<size_t>(r) * d + ch * VN, pk);
+        if (ho) st16(ho + static_cast<size_t>(r) * d + ch * VN, pk);
+      }
+      float g[VN], o[VN];
+      unpack(gq[u], g, T());
+#pragma unroll
+      for (int i = 0; i < VN; ++i) o[i] = round_to<T>((v[u][i] * inv[r]) * g[i]);
+      st16(A + r * lda + ch * VN, pack(o, T()));
+    }
+    for (int ch = tid; ch < nvec; ch += kRowThreads) st16(A + m * lda + ch * VN, make_uint4(0, 0, 0, 0));
+    __syncthreads();
+    const int arow = (lane & 15) < m ? (lane & 15) : m;
+    ls.finish(p, 0, m, A + arow * lda + (lane >> 4) * VN, red, tid);
+    return;
+  }
+  tile_inv_rms<VN>(m, d, a.eps, part, inv, hv);
   for (int it = tid; it < (m + 1) * nvec; it += blockDim.x) {
     const int r = it / nvec, ch = it - r * nvec;
     uint4 xo = make_uint4(0, 0, 0, 0);
