@@ -694,7 +694,7 @@ def _mean_commits(bd, torch, g, p, vocab, seed, n):
 
 
 def forced_parity(bd, torch, model, W, dims, h, B, K, pre, drafts_np, out):
-    """The oracle's verdict on the timed step, teacher-forced: the layer
+    """The oracle's check of the timed step, teacher-forced: the layer
     chain (moe_layer_forward, which reproduces the step's routing bit for
     bit) runs on the GPU, and each layer of the oracle is fed the GPU's input
     to that layer.  Counts routing decisions whose oracle margin is below
