@@ -45,22 +45,63 @@ __device__ __forceinline__ void load_batch(uint4 *q, const T *b, int w0, int w_h
   constexpr int W = 4 * Vec<T>::N;
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if (w0 + u < w_hi) q[u] = ld16(b + (w0 + u) * W);
+    if (w0 + u < w_hi) q[u] = gld16(b + (w0 + u) * W);
+}
+
+// U MFMAs over windows [w0, min(w0 + U, w_hi)), branch-free for a full batch.
+template <typename T, int U>
+__device__ __forceinline__ void mfma_batch(f32x4_t &acc, const T *a, const uint4 *q, int w0, int w_hi) {
+  constexpr int W = 4 * Vec<T>::N;
+  if (w0 + U <= w_hi) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+  }
 }
 
 // acc += A[16 x K] * B[K x 16] over windows [w_lo, w_hi), the first batch of
 // weights already in `q`: lane l reads A row (l % 16) from `a` (LDS) and B
 // column (l % 16) from `b` (global), both at K offset (l / 16) * VN inside
 // each window of 4*VN elements.
+//
+// Batches of up to kUnroll windows (w_lo and w_hi the same in every lane of
+// the wavefront): each later batch lives in registers of its own iteration,
+// so that no weight register is carried from one batch to the next (a
+// carried batch is copied as a whole, which waits for all of its loads before
+// the first MFMA), and a full batch is branch-free, each MFMA waiting for its
+// own load only.  Longer batches (the fused small-batch launch) keep one wait
+// per batch: there the per-window form needs more registers than three
+// blocks per compute unit leave, and measured slower.
 template <typename T, int U = kUnroll>
 __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
                                            uint4 *q) {
   constexpr int W = 4 * Vec<T>::N;
-  for (int w0 = w_lo; w0 < w_hi; w0 += U) {
-    if (w0 != w_lo) load_batch<T, U>(q, b, w0, w_hi);
+  if constexpr (U > kUnroll) {
+    for (int w0 = w_lo; w0 < w_hi; w0 += U) {
+      if (w0 != w_lo) load_batch<T, U>(q, b, w0, w_hi);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+      for (int u = 0; u < U; ++u)
+        if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
+    }
+    return;
+  }
+  if (w_lo >= w_hi) return;
+  mfma_batch<T, U>(acc, a, q, w_lo, w_hi);
+  for (int w0 = w_lo + U; w0 < w_hi; w0 += U) {
+    uint4 r[U];
+    if (w0 + U <= w_hi) {  // a full batch: loads and MFMAs in one branch-free block
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[u] = gld16(b + (w0 + u) * W);
+      __builtin_amdgcn_sched_barrier(0);  // every load of the batch in flight before the first MFMA
+#pragma unroll
+      for (int u = 0; u < U; ++u) mfma16(acc, ld16(a + (w0 + u) * W), r[u], T());
+    } else {
+      load_batch<T, U>(r, b, w0, w_hi);
+      mfma_batch<T, U>(acc, a, r, w0, w_hi);
+    }
   }
 }
 
@@ -69,12 +110,7 @@ __device__ __forceinline__ void mfma_panel(f32x4_t &acc, const T *a, const T *b,
 template <typename T, int U>
 __device__ __forceinline__ void mfma_panel2(f32x4_t &acc, const T *a, const T *b, int w_lo, int w_hi,
                                             uint4 *q0, uint4 *q1) {
-  constexpr int W = 4 * Vec<T>::N;
-  auto mma = [&](const uint4 *q, int w0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (w0 + u < w_hi) mfma16(acc, ld16(a + (w0 + u) * W), q[u], T());
-  };
+  auto mma = [&](const uint4 *q, int w0) { mfma_batch<T, U>(acc, a, q, w0, w_hi); };
   for (int w0 = w_lo; w0 < w_hi; w0 += 2 * U) {
     if (w0 + U < w_hi) load_batch<T, U>(q1, b, w0 + U, w_hi);
     mma(q0, w0);
@@ -101,10 +137,10 @@ __device__ __forceinline__ void stage_a_tile(const ExpertArgs &p, const TileInfo
       const T *src = a + static_cast<size_t>(ti.r0 + rr) * F + c * VN;
       if constexpr (kCoherent) {
         const uint32_t *q = reinterpret_cast<const uint32_t *>(src);
-        v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.x = ld_agent(q);
+        v.y = ld_agent(q + 1);
+        v.z = ld_agent(q + 2);
+        v.w = ld_agent(q + 3);
       } else {
         v = ld16(src);
       }
@@ -117,13 +153,12 @@ __device__ __forceinline__ void stage_a_tile(const ExpertArgs &p, const TileInfo
 // adjacent columns (bf16: the even lane stores both as one 32-bit word; both
 // lanes of the pair must call this).
 __device__ __forceinline__ void store_through(float *p, float v, int) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  st_agent(p, v);
 }
 __device__ __forceinline__ void store_through(bf16_t *p, float v, int lane) {
   const uint32_t mine = f32_to_bf16(v), other = __shfl_xor(mine, 1);
   if (!(lane & 1))
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), mine | (other << 16), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    st_agent(reinterpret_cast<uint32_t *>(p), mine | (other << 16));
 }
 
 // gate/up of slice pair `pair` of a tile.  begin() issues the first weight
@@ -150,6 +185,10 @@ struct GateUpPart {
     const int nwin = d / (4 * VN);
     w_lo = f0 < F ? ks * nwin / ns : 0;
     w_hi = f0 < F ? (ks + 1) * nwin / ns : 0;
+    if constexpr (U <= kUnroll) {  // the same in every lane: scalar branches in the stream
+      w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+      w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+    }
     const T *W = expert_base<T>(p, ti.e, static_cast<size_t>(2) * F * d);
     b = W + static_cast<size_t>(which * F + min(f0, F - 16) + r) * d + koff;
     load_batch<T, U>(q, b, w_lo, w_hi);
@@ -220,6 +259,10 @@ struct DownPart {
     const int nwin = F / (4 * VN), k0 = ks * nwin / ns, k1 = (ks + 1) * nwin / ns;
     w_lo = n0 < d ? k0 + half * (k1 - k0) / 2 : 0;
     w_hi = n0 < d ? k0 + (half + 1) * (k1 - k0) / 2 : 0;
+    if constexpr (U <= kUnroll) {  // the same in every lane: scalar branches in the stream
+      w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+      w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+    }
     const T *W = w_routed ? expert_base<T>(w_routed, w_shared, p.E, ti.e, static_cast<size_t>(d) * F)
                           : expert_base<T>(p, ti.e, static_cast<size_t>(d) * F);
     b = W + static_cast<size_t>(min(n0, d - 16) + r) * F + koff;
@@ -251,7 +294,7 @@ struct DownPart {
         const float w = s < p.k ? gates[tok * p.k + s] : 1.0f;
         float *dst = p.slots + out_off + static_cast<size_t>(pair) * d + n0 + (lane & 15);
         const float v = w * (acc[i] + half_acc[slice][lane][i]);
-        if constexpr (kThrough) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kThrough) st_agent(dst, v);
         else *dst = v;
       }
     }

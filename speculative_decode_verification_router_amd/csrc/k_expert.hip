@@ -74,10 +74,10 @@ __device__ void small_top_k_poll(const ExpertArgs &p, SmallTiles &st, bool selec
     const float *row = p.logits + static_cast<size_t>(t) * 64 + lane;
     float v = 0.f;
     for (int polls = 0;; ++polls) {
-      v = __hip_atomic_load(row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v = ld_agent(row);
       if (!__ballot(lane < p.E && __float_as_uint(v) == kLogitUnset)) break;
       if (polls >= p.spin_limit) {
-        if (lane == 0) __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) st_agent(p.err, 1u);
         break;
       }
       __builtin_amdgcn_s_sleep(64);
@@ -252,9 +252,9 @@ __device__ __forceinline__ void wait_count(const unsigned *ctr, unsigned target,
   if (threadIdx.x != 0) return;
   unsigned n = 0;
   int polls = 0;
-  while ((n = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target && polls++ < limit)
+  while ((n = ld_agent(ctr)) < target && polls++ < limit)
     __builtin_amdgcn_s_sleep(64);
-  if (n < target) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (n < target) st_agent(err, 1u);
 }
 
 // n_route > 0: the launch also routes this layer (ra, ca): its first n_route
@@ -340,10 +340,10 @@ __device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const 
         const T *src = x + static_cast<size_t>(st.rows[w][rr] / p.nslot) * d + c * VN;
         if (n_route) {
           const uint32_t *q = reinterpret_cast<const uint32_t *>(src);
-          v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.x = ld_agent(q);
+          v.y = ld_agent(q + 1);
+          v.z = ld_agent(q + 2);
+          v.w = ld_agent(q + 3);
         } else {
           v = ld16(src);
         }
@@ -355,7 +355,7 @@ __device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's products have completed
     __syncthreads();
     if (tid == 0)
-      __hip_atomic_fetch_add(p.tile_done + y * kDoneStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      add_agent(p.tile_done + y * kDoneStride, 1u);
     return;
   }
 
@@ -372,10 +372,10 @@ __device__ void ffn_small_block(const ExpertArgs &p, const RouteArgs &ra, const 
       uint4 v = make_uint4(0, 0, 0, 0);
       if (rr < ti.m) {
         const uint32_t *q = reinterpret_cast<const uint32_t *>(a + static_cast<size_t>(ti.r0 + rr) * F + c * VN);
-        v.x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.x = ld_agent(q);
+        v.y = ld_agent(q + 1);
+        v.z = ld_agent(q + 2);
+        v.w = ld_agent(q + 3);
       }
       if (rr < ti.m || rr == R) st16(A + rr * lda + c * VN, v);
     }
@@ -462,7 +462,7 @@ __device__ __forceinline__ void one_launch_lm_block(const LmArgs &p, int vblk, i
                                                              unsigned long long (*red)[kTileM]) {
   constexpr int VN = Vec<T>::N;
   const int tid = threadIdx.x, T_ = p.T, d = p.d;
-  LmStream<T> ls;
+  LmStream<T, true> ls;  // p is read from device memory
   ls.begin(p, vblk, tid);  // weights requested before x_f is ready
   wait_count(ready, static_cast<unsigned>(T_), err, spin_limit);
   __syncthreads();
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void k_one_launch(const OneLaunchDev *__r
     if (local >= n_route) {  // count this expert block of layer l
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // its slots have completed
       __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(done_l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) add_agent(done_l, 1u);
     }
     return;
   }
@@ -551,10 +551,10 @@ __device__ __forceinline__ void mid_chain(f32x4_t (*acc)[MT], const T *const *ar
       for (int i = 0; i < MT; ++i) qa[buf][i][u] = ld16(ar[i] + w * WIN);
     }
   };
-  if (w_lo >= w_hi) return;
-  load(0, w_lo);
-  int buf = 0;
-  for (int w0 = w_lo; w0 < w_hi; w0 += U, buf ^= 1) {
+  // batch at w0 in buffer `buf`, the next one requested into the other
+  // buffer first; two batches per iteration keep `buf` a compile-time index,
+  // so that both buffers stay in registers
+  auto step = [&](int buf, int w0) {
     if (w0 + U < w_hi) load(buf ^ 1, w0 + U);
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -564,6 +564,12 @@ __device__ __forceinline__ void mid_chain(f32x4_t (*acc)[MT], const T *const *ar
 #pragma unroll
           for (int c = 0; c < NB; ++c) mfma16(acc[c][i], qa[buf][i][u], qb[buf][c][u], T());
       }
+  };
+  if (w_lo >= w_hi) return;
+  load(0, w_lo);
+  for (int w0 = w_lo; w0 < w_hi; w0 += 2 * U) {
+    step(0, w0);
+    if (w0 + U < w_hi) step(1, w0 + U);
   }
 }
 

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_permute_large(RouteArgs p) {
 }
 
 __global__ void k_copy_status(const unsigned *word, int32_t *status) {
-  status[0] = static_cast<int32_t>(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  status[0] = static_cast<int32_t>(ld_agent(word));
 }
 
 }  // namespace

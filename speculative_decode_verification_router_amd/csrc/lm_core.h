@@ -16,8 +16,11 @@ constexpr int kLmRowsPerBlock = 16 * kLmSlices * kLmWaves;
 // wavefront streams its slices' weight rows as one sequence of batches of
 // kLmUnroll windows, the next batch requested before the current one is
 // multiplied; begin() requests the first batch, so a kernel can issue it
-// before it stages the x_f rows.
-template <typename T>
+// before it stages the x_f rows.  kGlobal: the weight loads go through a
+// global-space pointer (gld16), for callers whose arguments come from device
+// memory; elsewhere the compiler already knows the space, and the plain form
+// schedules better.
+template <typename T, bool kGlobal = false>
 struct LmStream {
   static constexpr int VN = Vec<T>::N, WIN = 4 * VN;
   int vbase, nwin, bps, nb, koff;
@@ -33,7 +36,7 @@ struct LmStream {
     const T *b = row(p, slice);
 #pragma unroll
     for (int u = 0; u < kLmUnroll; ++u)
-      if (w0 + u < nwin) q[u] = ld16(b + (w0 + u) * WIN);
+      if (w0 + u < nwin) q[u] = kGlobal ? gld16(b + (w0 + u) * WIN) : ld16(b + (w0 + u) * WIN);
   }
   __device__ __forceinline__ void begin(const LmArgs &p, int vblk, int tid) {
     const int lane = tid & 63, wv = tid >> 6;
@@ -111,7 +114,7 @@ __device__ inline void accept_sequence(const AcceptArgs &p, int b, bool coherent
     int g;
     if (p.argkey) {
       const unsigned long long key =
-          coherent ? __hip_atomic_load(p.argkey + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+          coherent ? ld_agent(p.argkey + base + j)
                    : p.argkey[base + j];
       g = static_cast<int>(key_index(key));
     } else {
@@ -137,7 +140,7 @@ __device__ inline void lm_block_done(const LmArgs &p, unsigned n_blocks) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_blocks - 1;
+    last = add_agent(p.done, 1u) == n_blocks - 1;
   __syncthreads();
   if (!last) return;
   for (int b = threadIdx.x; b < p.accept.B; b += blockDim.x) accept_sequence(p.accept, b, true);

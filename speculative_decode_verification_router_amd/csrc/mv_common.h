@@ -101,6 +101,31 @@ template <int N> __device__ __forceinline__ void st_f32(float *p, const float *v
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes of global memory through a global-space pointer: a global load
+// even where the compiler cannot tell the pointer's space (arguments read
+// from device memory), instead of a flat load, which counts on the LDS
+// counter too and so holds up every LDS wait while it is in flight.  The
+// load is of a vector type: a copy of uint4 would bind a flat reference.
+__device__ __forceinline__ uint4 gld16(const void *p) {
+  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t *)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Agent-scope relaxed atomics on global memory, through global-space
+// pointers for the same reason as gld16.
+template <typename V>
+__device__ __forceinline__ V ld_agent(const V *p) {
+  return __hip_atomic_load((const __attribute__((address_space(1))) V *)p, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ void st_agent(V *p, V v) {
+  __hip_atomic_store((__attribute__((address_space(1))) V *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V add_agent(V *p, V v) {
+  return __hip_atomic_fetch_add((__attribute__((address_space(1))) V *)p, v, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -111,18 +136,15 @@ __device__ __forceinline__ void st16(void *p, const uint4 &v) { *reinterpret_cas
 // agent-scope loads, which no stale cache line can answer.
 __device__ __forceinline__ uint4 ld16_agent(const void *p) {
   const uint32_t *q = static_cast<const uint32_t *>(p);
-  return make_uint4(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                    __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                    __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                    __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return make_uint4(ld_agent(q), ld_agent(q + 1), ld_agent(q + 2), ld_agent(q + 3));
 }
 // 16 bytes that other blocks of the same launch read: write-through stores.
 __device__ __forceinline__ void st16_through(void *p, const uint4 &v) {
   uint32_t *q = static_cast<uint32_t *>(p);
-  __hip_atomic_store(q, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  st_agent(q, v.x);
+  st_agent(q + 1, v.y);
+  st_agent(q + 2, v.z);
+  st_agent(q + 3, v.w);
 }
 
 // One 16x16 MFMA accumulation over the K-window that one 16-byte vector per

@@ -39,7 +39,7 @@ __device__ __forceinline__ void router_preload(uint4 *wq, const T *w_router, int
   const int nvec = d / VN;
 #pragma unroll
   for (int i = 0; i < kRouterChunks; ++i)
-    if (q + 16 * i < nvec) wq[i] = ld16(wr + (q + 16 * i) * VN);
+    if (q + 16 * i < nvec) wq[i] = gld16(wr + (q + 16 * i) * VN);
 }
 
 // Router logit (without bias) of expert e_base + lane / 16 for the x row at
@@ -63,7 +63,7 @@ __device__ __forceinline__ float router_dot(const uint4 *wq, const T *xr, int d,
 #pragma unroll
   for (int i = 0; i < kRouterChunks; ++i)
     if (q + 16 * i < nvec) accumulate(wq[i], q + 16 * i);
-  for (int c = q + 16 * kRouterChunks; c < nvec; c += 16) accumulate(ld16(wr + c * VN), c);
+  for (int c = q + 16 * kRouterChunks; c < nvec; c += 16) accumulate(gld16(wr + c * VN), c);
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
   return acc;
@@ -82,7 +82,7 @@ __device__ __forceinline__ void router_rows(const uint4 *wq, const T *x_lds, int
   for (int t = 0; t < nt; ++t) {
     const float acc = router_dot<T>(wq, x_lds + t * ldx, d, w_router, E, e_base);
     if (q == 0 && e < 64) {
-      if constexpr (kThrough) __hip_atomic_store(lg + t * 64 + e, acc + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (kThrough) st_agent(lg + t * 64 + e, acc + b);
       else lg[t * 64 + e] = acc + b;
     }
   }
@@ -139,7 +139,7 @@ template <bool kCoherent = false>
 __device__ __forceinline__ void select_top_k(const float *lg_row, uint64_t *key_lds, float *sel_lds, int E,
                                              int k, int *ids, float *gates, int *cnt_lds = nullptr) {
   const int lane = threadIdx.x & 63;
-  const float logit = kCoherent ? __hip_atomic_load(lg_row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+  const float logit = kCoherent ? ld_agent(lg_row + lane)
                                 : lg_row[lane];
   select_top_k_of(logit, key_lds, sel_lds, E, k, ids, gates, cnt_lds);
 }
@@ -338,7 +338,7 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
   auto slot4 = [](const float *p, float *o) {
     if constexpr (kInLaunch) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < 4; ++i) o[i] = ld_agent(p + i);
     } else {
       ld_f32<4>(p, o);
     }
@@ -416,14 +416,14 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
     st16(hl + ch * VN, pk);
     if (writer) {
       uint32_t *q = reinterpret_cast<uint32_t *>(xo + ch * VN);
-      __hip_atomic_store(q, pk.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(q + 1, pk.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(q + 2, pk.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(q + 3, pk.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_agent(q, pk.x);
+      st_agent(q + 1, pk.y);
+      st_agent(q + 2, pk.z);
+      st_agent(q + 3, pk.w);
     }
   }
   if constexpr (kFinal) {
-    if (tid == 0) __hip_atomic_store(a.argkey + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) st_agent(a.argkey + t, 0ull);
   } else if constexpr (!kInLaunch) {
     // the fused launch's readers take the logits as they land, so x must
     // have completed before any logit is stored; the wait overlaps the
@@ -438,7 +438,7 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's x has completed
     __syncthreads();
     if (router_wave && (lane & 15) == 0 && e < 64)
-      __hip_atomic_store(a.logits + static_cast<size_t>(t) * 64 + e, lg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_agent(a.logits + static_cast<size_t>(t) * 64 + e, lg);
     return;
   } else {
     __syncthreads();
@@ -449,7 +449,7 @@ __device__ void route_fused(const RouteArgs &a, const CombineArgs &c, int t, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's x and logits have completed
   __syncthreads();
   if (tid < copies)
-    __hip_atomic_fetch_add(done + static_cast<size_t>(tid) * stride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    add_agent(done + static_cast<size_t>(tid) * stride, 1u);
 }
 
 // ---------------------------------------------------------------- grouping
