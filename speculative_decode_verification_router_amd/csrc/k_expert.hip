@@ -526,14 +526,17 @@ __global__ __launch_bounds__(kThreads) void k_one_launch(const OneLaunchDev *__r
 
 // ------------------------------------------------------------ medium batches
 //
-// Tiles of up to MT * 16 rows of one expert and one wavefront per 16 output
-// columns, with no LDS: each wavefront reads its A fragments from global
-// memory (they stay in L2) next to its weight stream, so every weight row is
-// read once per tile instead of once per 16 rows.  Loads run one batch of
-// kMidWin windows ahead of the MFMAs.  Per-row arithmetic is the 16-row
+// Tiles of up to MT * 16 rows of one expert and one wavefront per
+// kMidSlices 16-column slices of the output, with no LDS: each wavefront
+// reads its A fragments from global memory (they stay in L2) next to its
+// weight stream and uses them for all of its slices, so every weight row is
+// read once per tile instead of once per 16 rows, and the A fragments once
+// per kMidSlices slices.  Loads run one batch of kMidWin windows ahead of the
+// MFMAs.  Per-row arithmetic is the 16-row
 // kernels': gate and up each one MFMA chain over K in window order; down two
 // chains over the K halves, added low half first.
 constexpr int kMidWin = 2;
+constexpr int kMidSlices = 2;  // 16-column weight slices per wavefront, sharing its A fragments
 
 // acc[c][i] += A_i * B_c over windows [w_lo, w_hi) for NB weight streams.
 template <typename T, int MT, int NB>
@@ -581,11 +584,16 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_mid(ExpertArgs p) {
   const int e = ti.e, r0 = ti.r0, m = ti.m;
   const int d = p.d, F = p.F;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int f0 = (blockIdx.x * (kThreads / kWave) + wv) * 16;
-  if (f0 >= F) return;  // no block-wide synchronisation below
+  const int f0 = (blockIdx.x * (kThreads / kWave) + wv) * 16 * kMidSlices;
+  if (f0 >= F) return;  // no block-wide synchronisation below (F % 64 == 0: every slice is inside)
   const int r = lane & 15, koff = (lane >> 4) * VN;
   const T *W = expert_base<T>(p, e, static_cast<size_t>(2) * F * d);
-  const T *b[2] = {W + static_cast<size_t>(f0 + r) * d + koff, W + static_cast<size_t>(F + f0 + r) * d + koff};
+  const T *b[2 * kMidSlices];  // [slice][gate | up]
+#pragma unroll
+  for (int c = 0; c < kMidSlices; ++c) {
+    b[2 * c] = W + static_cast<size_t>(f0 + 16 * c + r) * d + koff;
+    b[2 * c + 1] = W + static_cast<size_t>(F + f0 + 16 * c + r) * d + koff;
+  }
   const T *x = static_cast<const T *>(p.x);
   const T *ar[MT];
 #pragma unroll
@@ -594,25 +602,26 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_mid(ExpertArgs p) {
     const int pair = p.rows[r0 + (row < m ? row : 0)];
     ar[i] = x + static_cast<size_t>(pair / p.nslot) * d + koff;
   }
-  f32x4_t acc[2][MT];  // [gate | up][tile]
+  f32x4_t acc[2 * kMidSlices][MT];  // [slice][gate | up][tile]
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    acc[0][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc[1][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  mid_chain<T, MT, 2>(acc, ar, b, 0, d / WIN);
+  for (int c = 0; c < 2 * kMidSlices; ++c)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[c][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  mid_chain<T, MT, 2 * kMidSlices>(acc, ar, b, 0, d / WIN);
   T *aout = static_cast<T *>(p.a_out);
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+  for (int c = 0; c < kMidSlices; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = i * 16 + (lane >> 4) * 4 + j;
-      if (row < m) {
-        const float gv = acc[0][i][j], uv = acc[1][i][j];
-        aout[static_cast<size_t>(r0 + row) * F + f0 + r] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = i * 16 + (lane >> 4) * 4 + j;
+        if (row < m) {
+          const float gv = acc[2 * c][i][j], uv = acc[2 * c + 1][i][j];
+          aout[static_cast<size_t>(r0 + row) * F + f0 + 16 * c + r] = from_f32<T>(gv / (1.0f + expf(-gv)) * uv);
+        }
       }
     }
-  }
 }
 
 template <typename T, int MT>
@@ -623,10 +632,13 @@ __global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
   const int e = ti.e, r0 = ti.r0, m = ti.m;
   const int d = p.d, F = p.F;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * (kThreads / kWave) + wv) * 16;
-  if (n0 >= d) return;
+  const int n0 = (blockIdx.x * (kThreads / kWave) + wv) * 16 * kMidSlices;
+  if (n0 >= d) return;  // d % 64 == 0: every slice is inside
   const int r = lane & 15, koff = (lane >> 4) * VN;
-  const T *b[1] = {expert_base<T>(p, e, static_cast<size_t>(d) * F) + static_cast<size_t>(n0 + r) * F + koff};
+  const T *b[kMidSlices];
+#pragma unroll
+  for (int c = 0; c < kMidSlices; ++c)
+    b[c] = expert_base<T>(p, e, static_cast<size_t>(d) * F) + static_cast<size_t>(n0 + 16 * c + r) * F + koff;
   const T *a = static_cast<const T *>(p.a);
   const T *ar[MT];
 #pragma unroll
@@ -634,15 +646,17 @@ __global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
     const int row = i * 16 + r;
     ar[i] = a + static_cast<size_t>(r0 + (row < m ? row : 0)) * F + koff;
   }
-  f32x4_t lo[1][MT], hi[1][MT];
+  f32x4_t lo[kMidSlices][MT], hi[kMidSlices][MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    lo[0][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    hi[0][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int c = 0; c < kMidSlices; ++c)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      lo[c][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      hi[c][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
   const int nwin = F / WIN;
-  mid_chain<T, MT, 1>(lo, ar, b, 0, nwin / 2);
-  mid_chain<T, MT, 1>(hi, ar, b, nwin / 2, nwin);
+  mid_chain<T, MT, kMidSlices>(lo, ar, b, 0, nwin / 2);
+  mid_chain<T, MT, kMidSlices>(hi, ar, b, nwin / 2, nwin);
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -652,7 +666,9 @@ __global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
         const int pair = p.rows[r0 + row];
         const int tok = pair / p.nslot, s = pair - tok * p.nslot;
         const float w = s < p.k ? p.gates[tok * p.k + s] : 1.0f;
-        p.slots[static_cast<size_t>(pair) * d + n0 + r] = w * (lo[0][i][j] + hi[0][i][j]);
+#pragma unroll
+        for (int c = 0; c < kMidSlices; ++c)
+          p.slots[static_cast<size_t>(pair) * d + n0 + 16 * c + r] = w * (lo[c][i][j] + hi[c][i][j]);
       }
     }
   }
@@ -764,7 +780,7 @@ hipError_t launch_one_launch(int dtype, const OneLaunchArgs &a, OneLaunchDev *de
 namespace mv {
 
 hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  const dim3 grid((a.F + 63) / 64, max_tiles);
+  const dim3 grid((a.F + 64 * kMidSlices - 1) / (64 * kMidSlices), max_tiles);
   if (dtype == 1)
     hipLaunchKernelGGL((k_gate_up_mid<bf16_t, kMidTiles>), grid, dim3(kThreads), 0, s, a);
   else
@@ -773,7 +789,7 @@ hipError_t launch_gate_up_mid(int dtype, const ExpertArgs &a, int max_tiles, hip
 }
 
 hipError_t launch_down_mid(int dtype, const ExpertArgs &a, int max_tiles, hipStream_t s) {
-  const dim3 grid((a.d + 63) / 64, max_tiles);
+  const dim3 grid((a.d + 64 * kMidSlices - 1) / (64 * kMidSlices), max_tiles);
   if (dtype == 1)
     hipLaunchKernelGGL((k_down_mid<bf16_t, kMidTiles>), grid, dim3(kThreads), 0, s, a);
   else
