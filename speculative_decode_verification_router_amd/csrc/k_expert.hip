@@ -527,49 +527,76 @@ __global__ __launch_bounds__(kThreads) void k_one_launch(const OneLaunchDev *__r
 // ------------------------------------------------------------ medium batches
 //
 // Tiles of up to MT * 16 rows of one expert and one wavefront per
-// kMidSlices 16-column slices of the output, with no LDS: each wavefront
-// reads its A fragments from global memory (they stay in L2) next to its
-// weight stream and uses them for all of its slices, so every weight row is
-// read once per tile instead of once per 16 rows, and the A fragments once
-// per kMidSlices slices.  Loads run one batch of kMidWin windows ahead of the
-// MFMAs.  Per-row arithmetic is the 16-row
+// kMidSlices 16-column slices of the output: the block stages the tile's A
+// rows through LDS one batch of kMidWin windows at a time and each
+// wavefront uses its A fragments for all of its slices, so every weight row
+// is read once per tile instead of once per 16 rows.  Loads run one batch
+// ahead of the MFMAs.  Per-row arithmetic is the 16-row
 // kernels': gate and up each one MFMA chain over K in window order; down two
 // chains over the K halves, added low half first.
 constexpr int kMidWin = 2;
 constexpr int kMidSlices = 2;  // 16-column weight slices per wavefront, sharing its A fragments
 
 // acc[c][i] += A_i * B_c over windows [w_lo, w_hi) for NB weight streams.
+// The block's 16 * MT A rows are staged through LDS one batch of kMidWin
+// windows at a time: thread t loads 16 bytes of row t / 4 per window (srow:
+// that row at this thread's 16-byte part) and every wavefront reads its
+// fragments there, so a window costs one A load per lane instead of MT.
+// Every wavefront of the block must call this with the same window range
+// (one barrier per batch).
+template <typename T, int MT>
+constexpr int mid_lds_bytes() {
+  return 2 * kMidWin * 16 * MT * (4 * Vec<T>::N * static_cast<int>(sizeof(T)) + 16);
+}
 template <typename T, int MT, int NB>
-__device__ __forceinline__ void mid_chain(f32x4_t (*acc)[MT], const T *const *ar, const T *const *b,
-                                          int w_lo, int w_hi) {
+__device__ __forceinline__ void mid_chain(f32x4_t (*acc)[MT], const T *srow, const T *const *b, int w_lo,
+                                          int w_hi, unsigned char *lds) {
   constexpr int WIN = 4 * Vec<T>::N, U = kMidWin;
-  uint4 qb[2][NB][U], qa[2][MT][U];
+  constexpr int RS = WIN * static_cast<int>(sizeof(T)) + 16;  // LDS row stride: one 16-byte pad
+  constexpr int SLAB = 16 * MT * RS, BUF = U * SLAB;            // one window, one batch
+  static_assert(16 * MT * 4 == kThreads, "one A row part per thread and window");
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned char *wr = lds + (tid >> 2) * RS + (tid & 3) * 16;
+  const unsigned char *rd = lds + (lane & 15) * RS + (lane >> 4) * 16;
+  uint4 qb[2][NB][U], sa[U];
+  // A parts first: staging them then waits for those loads only
   auto load = [&](int buf, int w0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) sa[u] = ld16(srow + min(w0 + u, w_hi - 1) * WIN);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int w = min(w0 + u, w_hi - 1);
 #pragma unroll
       for (int c = 0; c < NB; ++c) qb[buf][c][u] = ld16(b[c] + w * WIN);
-#pragma unroll
-      for (int i = 0; i < MT; ++i) qa[buf][i][u] = ld16(ar[i] + w * WIN);
     }
   };
-  // batch at w0 in buffer `buf`, the next one requested into the other
-  // buffer first; two batches per iteration keep `buf` a compile-time index,
-  // so that both buffers stay in registers
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) st16(wr + buf * BUF + u * SLAB, sa[u]);
+  };
+  // batch at w0 in buffer `buf` (registers and LDS), the next one requested
+  // into the other buffer first; two batches per iteration keep `buf` a
+  // compile-time index, so that both register buffers stay in registers
   auto step = [&](int buf, int w0) {
-    if (w0 + U < w_hi) load(buf ^ 1, w0 + U);
+    const bool more = w0 + U < w_hi;
+    if (more) load(buf ^ 1, w0 + U);
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (w0 + u < w_hi) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i) {
+          const uint4 a = ld16(rd + buf * BUF + u * SLAB + i * 16 * RS);
 #pragma unroll
-          for (int c = 0; c < NB; ++c) mfma16(acc[c][i], qa[buf][i][u], qb[buf][c][u], T());
+          for (int c = 0; c < NB; ++c) mfma16(acc[c][i], a, qb[buf][c][u], T());
+        }
       }
+    if (more) stage(buf ^ 1);
+    __syncthreads();  // the other buffer is staged; this one is free again
   };
   if (w_lo >= w_hi) return;
   load(0, w_lo);
+  stage(0);
+  __syncthreads();
   for (int w0 = w_lo; w0 < w_hi; w0 += 2 * U) {
     step(0, w0);
     if (w0 + U < w_hi) step(1, w0 + U);
@@ -584,30 +611,30 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_mid(ExpertArgs p) {
   const int e = ti.e, r0 = ti.r0, m = ti.m;
   const int d = p.d, F = p.F;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ __align__(16) unsigned char lds[mid_lds_bytes<T, MT>()];
   const int f0 = (blockIdx.x * (kThreads / kWave) + wv) * 16 * kMidSlices;
-  if (f0 >= F) return;  // no block-wide synchronisation below (F % 64 == 0: every slice is inside)
+  // a wavefront past F (F % 64 == 0: all of its slices are) streams the last
+  // slices again for the block's barriers and stores nothing
+  const int fw = min(f0, F - 16 * kMidSlices);
   const int r = lane & 15, koff = (lane >> 4) * VN;
   const T *W = expert_base<T>(p, e, static_cast<size_t>(2) * F * d);
   const T *b[2 * kMidSlices];  // [slice][gate | up]
 #pragma unroll
   for (int c = 0; c < kMidSlices; ++c) {
-    b[2 * c] = W + static_cast<size_t>(f0 + 16 * c + r) * d + koff;
-    b[2 * c + 1] = W + static_cast<size_t>(F + f0 + 16 * c + r) * d + koff;
+    b[2 * c] = W + static_cast<size_t>(fw + 16 * c + r) * d + koff;
+    b[2 * c + 1] = W + static_cast<size_t>(F + fw + 16 * c + r) * d + koff;
   }
   const T *x = static_cast<const T *>(p.x);
-  const T *ar[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int row = i * 16 + r;
-    const int pair = p.rows[r0 + (row < m ? row : 0)];
-    ar[i] = x + static_cast<size_t>(pair / p.nslot) * d + koff;
-  }
+  const int srow_i = threadIdx.x >> 2;  // this thread's staging row and part
+  const int spair = p.rows[r0 + (srow_i < m ? srow_i : 0)];
+  const T *srow = x + static_cast<size_t>(spair / p.nslot) * d + (threadIdx.x & 3) * VN;
   f32x4_t acc[2 * kMidSlices][MT];  // [slice][gate | up][tile]
 #pragma unroll
   for (int c = 0; c < 2 * kMidSlices; ++c)
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[c][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  mid_chain<T, MT, 2 * kMidSlices>(acc, ar, b, 0, d / WIN);
+  mid_chain<T, MT, 2 * kMidSlices>(acc, srow, b, 0, d / WIN, lds);
+  if (f0 >= F) return;
   T *aout = static_cast<T *>(p.a_out);
 #pragma unroll
   for (int c = 0; c < kMidSlices; ++c)
@@ -632,20 +659,17 @@ __global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
   const int e = ti.e, r0 = ti.r0, m = ti.m;
   const int d = p.d, F = p.F;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ __align__(16) unsigned char lds[mid_lds_bytes<T, MT>()];
   const int n0 = (blockIdx.x * (kThreads / kWave) + wv) * 16 * kMidSlices;
-  if (n0 >= d) return;  // d % 64 == 0: every slice is inside
+  const int nw = min(n0, d - 16 * kMidSlices);  // past d (d % 64 == 0): the last slices again, no stores
   const int r = lane & 15, koff = (lane >> 4) * VN;
   const T *b[kMidSlices];
 #pragma unroll
   for (int c = 0; c < kMidSlices; ++c)
-    b[c] = expert_base<T>(p, e, static_cast<size_t>(d) * F) + static_cast<size_t>(n0 + 16 * c + r) * F + koff;
+    b[c] = expert_base<T>(p, e, static_cast<size_t>(d) * F) + static_cast<size_t>(nw + 16 * c + r) * F + koff;
   const T *a = static_cast<const T *>(p.a);
-  const T *ar[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int row = i * 16 + r;
-    ar[i] = a + static_cast<size_t>(r0 + (row < m ? row : 0)) * F + koff;
-  }
+  const int srow_i = threadIdx.x >> 2;  // this thread's staging row and part
+  const T *srow = a + static_cast<size_t>(r0 + (srow_i < m ? srow_i : 0)) * F + (threadIdx.x & 3) * VN;
   f32x4_t lo[kMidSlices][MT], hi[kMidSlices][MT];
 #pragma unroll
   for (int c = 0; c < kMidSlices; ++c)
@@ -655,8 +679,9 @@ __global__ __launch_bounds__(kThreads) void k_down_mid(ExpertArgs p) {
       hi[c][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   const int nwin = F / WIN;
-  mid_chain<T, MT, kMidSlices>(lo, ar, b, 0, nwin / 2);
-  mid_chain<T, MT, kMidSlices>(hi, ar, b, nwin / 2, nwin);
+  mid_chain<T, MT, kMidSlices>(lo, srow, b, 0, nwin / 2, lds);
+  mid_chain<T, MT, kMidSlices>(hi, srow, b, nwin / 2, nwin, lds);
+  if (n0 >= d) return;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
