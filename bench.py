@@ -28,9 +28,9 @@ METRIC = "committed tokens/s (12-layer MoE verify, K=3) + % of HBM/MFMA roofline
 # profiles/verify_step_{b1,c32}_k3_hbm_counters.txt, profiles/mtp_draft_b1_k3_hbm_counters.txt)
 # on the kernel sources whose code (comments aside) has this digest; reported
 # only while the code matches.
-MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "d291ff574c96a72e", "bytes_per_step": 2.1845e9},
-                    "c32_k3": {"csrc_sha256_16": "d291ff574c96a72e", "bytes_per_step": 6.4236e9},
-                    "b1_k3_draft": {"csrc_sha256_16": "d291ff574c96a72e", "bytes_per_step": 1.0586e9}}
+MEASURED_TRAFFIC = {"b1_k3": {"csrc_sha256_16": "c7b7512a5d65c16d", "bytes_per_step": 2.1844e9},
+                    "c32_k3": {"csrc_sha256_16": "c7b7512a5d65c16d", "bytes_per_step": 6.4241e9},
+                    "b1_k3_draft": {"csrc_sha256_16": "c7b7512a5d65c16d", "bytes_per_step": 1.0586e9}}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
